@@ -1,0 +1,282 @@
+"""Oracle: split attention forward and backward, as NON-deduplicated attention.
+
+Test infrastructure only; see the package docstring.
+
+What it computes (How Prompt Deduplication Works -- Phase 2, Split Attention
+Optimization; Correctness & Gradients): in the packed batch every unique
+prompt attends causally to itself once, and each response attends to all of
+its prompt's keys plus its own causal prefix.  The pages require this to equal
+the ordinary, non-deduplicated computation ("Performance Benchmarks" --
+Testing Correctness and Performance: outputs and gradients are validated
+against a non-deduplicated reference).  So the oracle runs plain causal
+softmax attention separately on every sample's own ``[prompt][response]``
+sequence (gathered from the packed rows), in fp64, and maps the results
+back onto the packed rows:
+
+* forward -- response rows take their sample's output; prompt rows take the
+  output of the group's first member, and every other member's prompt
+  output is asserted equal to it (the deduplication invariant);
+* backward -- the gradient w.r.t. the packed tensors of
+  ``O_packed = assemble(attention of every sample)``: each sample's ``dO``
+  is the packed ``dO`` on its response rows and, on its prompt rows, the
+  packed ``dO`` for the group's first member and 0 for the others (prompt
+  outputs were taken from the first member only); per-sample textbook
+  gradients are scatter-added onto the packed rows, so prompt keys and
+  values collect the gradient of every response that reads them.
+
+Readings (the pages leave these open): softmax scale ``1/sqrt(head_dim)``
+unless given; query head ``h`` reads kv head ``h // (Hq // Hkv)``; a
+response row ``i`` sees every prompt key and its own keys ``0..i`` (never a
+sibling response); LSE is the natural log of the softmax denominator,
+``[Hq, T]``.
+
+Softmax rows are processed in blocks of query rows, each block over the keys
+``[0, block_end)``: the causal extent itself, no reordering of the sums
+beyond what a matrix product does.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .dedup import sample_rows
+
+_BLOCK = 512
+
+
+def _kv_head(h, Hq, Hkv):
+    return h // (Hq // Hkv)
+
+
+def _causal_block(Qs, Ks, Vs, i0, i1, scale, dOs=None):
+    """Plain causal softmax attention for query rows ``[i0, i1)`` of one sequence.
+
+    Query ``i`` sees keys ``0..i``.  Returns ``(p, o, lse)`` and, when
+    ``dOs`` is given, also ``dS`` (the softmax-input gradient, before the
+    scale), following the textbook derivation:
+    ``D = rowsum(dO * O)``, ``dP = dO V^T``, ``dS = P * (dP - D)``.
+    """
+    s = scale * (Qs[i0:i1] @ Ks[:i1].T)
+    future = np.arange(i1)[None, :] > np.arange(i0, i1)[:, None]
+    s[future] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    o = p @ Vs[:i1]
+    lse = (m + np.log(l))[:, 0]
+    if dOs is None:
+        return p, o, lse, None
+    dO = dOs[i0:i1]
+    D = (dO * o).sum(axis=1, keepdims=True)
+    dP = dO @ Vs[:i1].T
+    dS = p * (dP - D)
+    return p, o, lse, dS
+
+
+def _prep(q, k, v, scale):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return q, k, v, T, Hq, Hkv, d, float(scale)
+
+
+def _members_rep_first(info, g):
+    r = int(info["rep"][g])
+    return [r] + [b for b in info["groups"][g] if b != r]
+
+
+def split_attention_forward(q, k, v, info, scale=None, heads=None):
+    """Split attention forward over packed ``q [T,Hq,d]``, ``k, v [T,Hkv,d]``.
+
+    Returns ``o [T,Hq,d]`` and ``lse [Hq,T]`` (fp64).  ``heads`` restricts
+    the work to some query heads (others are left 0).
+    """
+    q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
+    heads = range(Hq) if heads is None else heads
+    o = np.zeros((T, Hq, d))
+    lse = np.zeros((Hq, T))
+    for g in range(info["G"]):
+        pl = int(info["prompt_len"][g])
+        rep = int(info["rep"][g])
+        for b in _members_rep_first(info, g):
+            idx = sample_rows(info, b)
+            L = len(idx)
+            for h in heads:
+                j = _kv_head(h, Hq, Hkv)
+                Qs, Ks, Vs = q[idx, h], k[idx, j], v[idx, j]
+                Ob = np.zeros((L, d))
+                Lb = np.zeros(L)
+                for i0 in range(0, L, _BLOCK):
+                    i1 = min(L, i0 + _BLOCK)
+                    _, Ob[i0:i1], Lb[i0:i1], _ = _causal_block(Qs, Ks, Vs, i0, i1, scale)
+                o[idx[pl:], h] = Ob[pl:]
+                lse[h, idx[pl:]] = Lb[pl:]
+                if b == rep:
+                    o[idx[:pl], h] = Ob[:pl]
+                    lse[h, idx[:pl]] = Lb[:pl]
+                else:
+                    # every copy of a prompt must produce the same prompt output
+                    err = np.max(np.abs(o[idx[:pl], h] - Ob[:pl]), initial=0.0)
+                    assert err <= 1e-12, f"prompt copies disagree by {err}"
+    return o, lse
+
+
+def split_attention_backward(q, k, v, dout, info, scale=None):
+    """Gradients ``(dq, dk, dv)`` of the packed split-attention output.
+
+    Per sample: textbook causal-attention backward with that sample's
+    ``dO`` (see the module docstring), then scatter-add onto packed rows;
+    query heads sharing a kv head add into it.
+    """
+    q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
+    dout = np.asarray(dout, dtype=np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for g in range(info["G"]):
+        pl = int(info["prompt_len"][g])
+        rep = int(info["rep"][g])
+        for b in _members_rep_first(info, g):
+            idx = sample_rows(info, b)
+            L = len(idx)
+            for h in range(Hq):
+                j = _kv_head(h, Hq, Hkv)
+                Qs, Ks, Vs = q[idx, h], k[idx, j], v[idx, j]
+                dOs = dout[idx, h].copy()
+                if b != rep:
+                    dOs[:pl] = 0.0
+                dQb = np.zeros((L, d))
+                dKb = np.zeros((L, d))
+                dVb = np.zeros((L, d))
+                for i0 in range(0, L, _BLOCK):
+                    i1 = min(L, i0 + _BLOCK)
+                    p, _, _, dS = _causal_block(Qs, Ks, Vs, i0, i1, scale, dOs)
+                    dVb[:i1] += p.T @ dOs[i0:i1]
+                    dQb[i0:i1] = scale * (dS @ Ks[:i1])
+                    dKb[:i1] += scale * (dS.T @ Qs[i0:i1])
+                dq[idx, h] += dQb
+                dk[idx, j] += dKb
+                dv[idx, j] += dVb
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Row-sampled versions for full-size checks: the same definition, evaluated
+# only where asked.  A packed row is located in the sequence of the sample
+# that owns it (the group's first member for prompt rows).
+# ---------------------------------------------------------------------------
+
+def _locate(info, j):
+    """(sample, position in that sample's sequence, is_prompt) of packed row ``j``."""
+    S, P = info["S"], info["P"]
+    src = int(info["src"][j])
+    b0, t = divmod(src, S)
+    g = int(info["group_of"][b0])
+    if t < P:
+        return int(info["rep"][g]), j - int(info["prompt_off"][g]), True
+    return b0, int(info["prompt_len"][g]) + (j - int(info["resp_off"][b0])), False
+
+
+def forward_rows(q, k, v, info, rows, heads, scale=None):
+    """Forward output and LSE for the listed packed rows and query heads.
+
+    Returns ``o [len(rows), len(heads), d]``, ``lse [len(rows), len(heads)]``.
+    """
+    q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
+    o = np.zeros((len(rows), len(heads), d))
+    lse = np.zeros((len(rows), len(heads)))
+    for a, j in enumerate(rows):
+        b, i, _ = _locate(info, int(j))
+        idx = sample_rows(info, b)
+        for c, h in enumerate(heads):
+            kv = _kv_head(h, Hq, Hkv)
+            _, ob, lb, _ = _causal_block(q[idx, h], k[idx, kv], v[idx, kv], i, i + 1, scale)
+            o[a, c] = ob[0]
+            lse[a, c] = lb[0]
+    return o, lse
+
+
+def dq_rows(q, k, v, dout, info, rows, heads, scale=None):
+    """``dq`` for the listed packed rows and query heads (``[len(rows), len(heads), d]``).
+
+    Only the owning sample has a non-zero ``dO`` on a row (prompt rows: the
+    group's first member), so the row's gradient is that sample's.
+    """
+    q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
+    dout = np.asarray(dout, dtype=np.float64)
+    out = np.zeros((len(rows), len(heads), d))
+    for a, j in enumerate(rows):
+        b, i, _ = _locate(info, int(j))
+        idx = sample_rows(info, b)
+        for c, h in enumerate(heads):
+            kv = _kv_head(h, Hq, Hkv)
+            Ks = k[idx, kv]
+            _, _, _, dS = _causal_block(q[idx, h], Ks, v[idx, kv], i, i + 1, scale, dout[idx, h])
+            out[a, c] = scale * (dS @ Ks[:i + 1])[0]
+    return out
+
+
+def dkdv_rows(q, k, v, dout, info, keys, kv_heads, scale=None):
+    """``dk, dv`` for the listed packed key rows and kv heads.
+
+    Sums, over every sample whose sequence contains the key and every query
+    position at or after it with a non-zero ``dO``, over the query heads of
+    the kv head: ``dv += P dO`` and ``dk += scale * dS q``.
+    """
+    q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
+    dout = np.asarray(dout, dtype=np.float64)
+    ratio = Hq // Hkv
+    dk = np.zeros((len(keys), len(kv_heads), d))
+    dv = np.zeros((len(keys), len(kv_heads), d))
+    for a, kr in enumerate(keys):
+        kr = int(kr)
+        b0, kpos, is_prompt = _locate(info, kr)
+        g = int(info["group_of"][b0])
+        pl = int(info["prompt_len"][g])
+        rep = int(info["rep"][g])
+        samples = _members_rep_first(info, g) if is_prompt else [b0]
+        for b in samples:
+            idx = sample_rows(info, b)
+            L = len(idx)
+            # query positions that see this key and carry a non-zero dO
+            first = kpos if (b == rep or not is_prompt) else pl
+            for c, j in enumerate(kv_heads):
+                for h in range(j * ratio, (j + 1) * ratio):
+                    Qs, Ks, Vs = q[idx, h], k[idx, j], v[idx, j]
+                    dOs = dout[idx, h].copy()
+                    if b != rep:
+                        dOs[:pl] = 0.0
+                    for i0 in range(first, L, _BLOCK):
+                        i1 = min(L, i0 + _BLOCK)
+                        p, _, _, dS = _causal_block(Qs, Ks, Vs, i0, i1, scale, dOs)
+                        dv[a, c] += p[:, kpos] @ dOs[i0:i1]
+                        dk[a, c] += scale * (dS[:, kpos] @ Qs[i0:i1])
+    return dk, dv
+
+
+def attended_pairs(info):
+    """Number of (query, key) pairs split attention evaluates on the packed batch.
+
+    Prompt ``g``: ``Pl (Pl + 1) / 2`` causal pairs once; response ``b``:
+    ``Rl * Pl`` prompt keys plus ``Rl (Rl + 1) / 2`` causal own pairs.
+    Also returns the non-deduplicated count, ``sum_b L_b (L_b + 1) / 2``.
+    """
+    dedup = 0
+    plain = 0
+    for g in range(info["G"]):
+        pl = int(info["prompt_len"][g])
+        dedup += pl * (pl + 1) // 2
+        for b in info["groups"][g]:
+            rl = int(info["resp_len"][b])
+            dedup += rl * pl + rl * (rl + 1) // 2
+            L = pl + rl
+            plain += L * (L + 1) // 2
+    return dedup, plain

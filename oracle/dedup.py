@@ -1,0 +1,187 @@
+"""Oracle: grouping, packing and reconstruction (exact integer work).
+
+Test infrastructure only; see the package docstring.
+
+Readings of the pages where they leave a step open (also listed in the
+design notes of the repository):
+
+* prompt region: the first ``S - response_length`` columns of every row
+  (Finding Prompt Groups only says ``response_length`` is the length of the
+  response portion);
+* grouping key: exact equality of those prompt token ids, pad ids included
+  (``find_prompt_groups`` takes no mask);
+* order: groups in order of first occurrence, members ascending -- the
+  pages' example ``[[0, 1], [2, 3]]`` is consistent with it;
+* the prompt copy that is packed, and whose positions and mask are used, is
+  the group's first member;
+* positions are gathered from ``position_ids``, not renumbered;
+* unpad keeps exactly the tokens whose mask is non-zero; reconstruction
+  writes 0 where no packed token maps;
+* a group whose members' responses are all padding still packs its prompt,
+  and a sample with an all-pad response owns no packed rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def find_prompt_groups(input_ids: np.ndarray, response_length: int):
+    """How Prompt Deduplication Works -- Core Algorithm, Finding Prompt Groups.
+
+    Partition the samples into lists of indices whose prompt tokens are
+    identical.  Brute force: every sample is compared token by token with the
+    first member of each group found so far.
+
+    Returns ``(prompt_groups, unique_prompts)`` with ``unique_prompts`` of
+    shape ``[num_unique, prompt_len]``.
+    """
+    ids = np.asarray(input_ids)
+    B, S = ids.shape
+    P = S - int(response_length)
+    if not (0 <= P <= S):
+        raise ValueError("response_length must be in [0, seq_len]")
+    groups: list[list[int]] = []
+    for b in range(B):
+        for members in groups:
+            if np.array_equal(ids[b, :P], ids[members[0], :P]):
+                members.append(b)
+                break
+        else:
+            groups.append([b])
+    unique_prompts = np.stack([ids[m[0], :P] for m in groups]) if groups else \
+        np.zeros((0, P), dtype=ids.dtype)
+    return groups, unique_prompts
+
+
+def create_deduplicated_batch(input_ids, position_ids, response_length, prompt_groups,
+                              unique_prompts, attention_mask=None, use_unpad=False):
+    """How Prompt Deduplication Works -- Creating Deduplicated Batch; Working with
+    Packed/Unpacked Sequences.
+
+    Builds ``[Prompt_1][Response_1_1][Response_1_2]...[Prompt_2][Response_2_1]...``
+    as one ``[1, T]`` sequence of ids and of positions, plus the metadata that
+    maps it back.  With ``use_unpad`` tokens whose mask is 0 are dropped.
+
+    ``info`` (the pages' reconstruction metadata, whose fields they leave
+    unspecified) holds, per group ``g``: ``prompt_off[g]``, ``prompt_len[g]``,
+    ``rep[g]``; per sample ``b``: ``group_of[b]``, ``resp_off[b]``,
+    ``resp_len[b]``, ``prompt_cols[b]``/``resp_cols[b]`` (the original columns
+    kept, in order); and ``src[T]`` (packed row -> ``b*S + t``), ``dst[B*S]``
+    ((b, t) -> packed row, or -1), ``seg_start[T]`` (first packed row of the
+    segment each packed row lies in).
+    """
+    ids = np.asarray(input_ids)
+    pos = np.asarray(position_ids)
+    B, S = ids.shape
+    P = S - int(response_length)
+    if use_unpad:
+        if attention_mask is None:
+            raise ValueError("use_unpad needs attention_mask")
+        keep = np.asarray(attention_mask) != 0
+    else:
+        keep = np.ones((B, S), dtype=bool)
+
+    src: list[int] = []
+    seg_start: list[int] = []
+    G = len(prompt_groups)
+    prompt_off = np.zeros(G, np.int64)
+    prompt_len = np.zeros(G, np.int64)
+    rep = np.zeros(G, np.int64)
+    group_of = np.full(B, -1, np.int64)
+    resp_off = np.zeros(B, np.int64)
+    resp_len = np.zeros(B, np.int64)
+    prompt_cols = [None] * B
+    resp_cols = [None] * B
+    for g, members in enumerate(prompt_groups):
+        r = members[0]
+        rep[g] = r
+        cols = np.flatnonzero(keep[r, :P])
+        prompt_off[g] = len(src)
+        prompt_len[g] = len(cols)
+        src.extend(int(r * S + t) for t in cols)
+        seg_start.extend([int(prompt_off[g])] * len(cols))
+        for b in members:
+            group_of[b] = g
+            prompt_cols[b] = cols
+            rcols = P + np.flatnonzero(keep[b, P:])
+            resp_off[b] = len(src)
+            resp_len[b] = len(rcols)
+            resp_cols[b] = rcols
+            src.extend(int(b * S + t) for t in rcols)
+            seg_start.extend([int(resp_off[b])] * len(rcols))
+    src_a = np.asarray(src, dtype=np.int64)
+    T = len(src_a)
+    dst = np.full(B * S, -1, np.int64)
+    for b in range(B):
+        g = group_of[b]
+        dst[b * S + prompt_cols[b]] = prompt_off[g] + np.arange(prompt_len[g])
+        dst[b * S + resp_cols[b]] = resp_off[b] + np.arange(resp_len[b])
+    flat_ids = ids.reshape(-1)
+    flat_pos = pos.reshape(-1)
+    dedup_ids = flat_ids[src_a].reshape(1, T)
+    dedup_pos = flat_pos[src_a].reshape(1, T)
+    info = dict(B=B, S=S, P=P, G=G, T=T, groups=[list(m) for m in prompt_groups],
+                rep=rep, group_of=group_of, prompt_off=prompt_off, prompt_len=prompt_len,
+                resp_off=resp_off, resp_len=resp_len, prompt_cols=prompt_cols,
+                resp_cols=resp_cols, src=src_a, dst=dst,
+                seg_start=np.asarray(seg_start, dtype=np.int64))
+    return dedup_ids, dedup_pos, info
+
+
+def reconstruct_sequences(dedup_hidden, info):
+    """How Prompt Deduplication Works -- Reconstructing Original Batch; Phase 3.
+
+    For each output sample copy its unique prompt, then its own response
+    tokens, to the columns they came from; every other position is 0.
+    Accepts ``[1, T, H]`` or ``[T, H]``; returns ``[B, S, H]``.
+    """
+    x = np.asarray(dedup_hidden)
+    if x.ndim == 3:
+        x = x[0]
+    B, S = info["B"], info["S"]
+    out = np.zeros((B, S) + x.shape[1:], dtype=x.dtype)
+    for b in range(B):
+        g = info["group_of"][b]
+        po, pl = info["prompt_off"][g], info["prompt_len"][g]
+        out[b, info["prompt_cols"][b]] = x[po:po + pl]
+        ro, rl = info["resp_off"][b], info["resp_len"][b]
+        out[b, info["resp_cols"][b]] = x[ro:ro + rl]
+    return out
+
+
+def pack_rows(rows, info):
+    """The deduplicated layout applied to per-token rows ``[B, S, W] -> [T, W]``.
+
+    Packed row ``j`` is the row of the token it was made from
+    (Creating Deduplicated Batch: each unique prompt once, then its responses).
+    """
+    x = np.asarray(rows)
+    B, S = info["B"], info["S"]
+    flat = x.reshape((B * S,) + x.shape[2:])
+    return flat[info["src"]]
+
+
+def sample_rows(info, b):
+    """Packed rows of sample ``b``'s own sequence: its group's prompt, then its response.
+
+    This is the non-deduplicated ``[Prompt][Response]`` sample expressed as
+    packed row indices (Phase 1 diagram: every sample is its prompt followed
+    by its response).
+    """
+    g = info["group_of"][b]
+    po, pl = info["prompt_off"][g], info["prompt_len"][g]
+    ro, rl = info["resp_off"][b], info["resp_len"][b]
+    return np.concatenate([np.arange(po, po + pl), np.arange(ro, ro + rl)]).astype(np.int64)
+
+
+def redundancy_counts(info):
+    """Performance Benchmarks -- Redundancy Analysis: total vs unique tokens.
+
+    ``total`` counts every sample's prompt and response tokens (the
+    non-deduplicated batch), ``unique`` counts the packed tokens, and
+    ``redundancy = 1 - unique / total``.
+    """
+    total = int(sum(info["prompt_len"][info["group_of"][b]] + info["resp_len"][b]
+                    for b in range(info["B"])))
+    unique = int(info["T"])
+    return total, unique, (1.0 - unique / total) if total else 0.0

@@ -1,0 +1,288 @@
+"""Pins for the oracle's split attention (CPU only).
+
+The oracle is tied to things other than itself:
+  * a library attention routine (torch scaled_dot_product_attention, fp64,
+    causal) run per sample, and torch.autograd through the packed-output
+    function built from it;
+  * special cases that reduce to plain causal attention;
+  * closed forms (constant V, zero Q, the first row);
+  * fp64 central finite differences;
+  * exact invariants of softmax attention gradients;
+  * brute-force pair counting.
+A few tests plant a mistake in the oracle (monkeypatched, CPU only) and check
+that the pins catch it.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import oracle.attention as oatt
+from workloads import WORKLOADS, make_attn_inputs, make_batch
+
+
+def _setup(w, permute=False, seed=None):
+    bt = make_batch(w, permute=permute)
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    _, _, info = oracle.create_deduplicated_batch(
+        bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
+        attention_mask=bt.attention_mask, use_unpad=w.use_unpad)
+    x = make_attn_inputs(w, info["T"])
+    return info, x
+
+
+SMALL = {
+    "tiny": WORKLOADS["tiny_fp32"],
+    "gqa_ragged_unpad": WORKLOADS["tiny_fp32"].scaled(
+        name="gqa_ragged_unpad", num_prompts=3, rollout_n=3, prompt_len=37, response_len=21,
+        num_q_heads=4, num_kv_heads=2, head_dim=16, resp_len_range=(0, 21), seed=77),
+    "mha": WORKLOADS["tiny_fp32"].scaled(name="mha", num_q_heads=3, num_kv_heads=3, head_dim=8,
+                                         prompt_len=20, response_len=9, seed=78),
+}
+
+
+def _sdpa_packed(q, k, v, info, scale):
+    """Packed output assembled from per-sample torch SDPA (fp64, causal, kv heads repeated)."""
+    T, Hq, d = q.shape
+    ratio = Hq // k.shape[1]
+    outs = []
+    for b in range(info["B"]):
+        idx = torch.as_tensor(oracle.sample_rows(info, b))
+        Q = q[idx].transpose(0, 1)
+        K = k[idx].repeat_interleave(ratio, dim=1).transpose(0, 1)
+        V = v[idx].repeat_interleave(ratio, dim=1).transpose(0, 1)
+        outs.append((idx, F.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=scale)
+                     .transpose(0, 1)))
+    o = torch.zeros_like(q)
+    out_rows = [None] * T
+    for b, (idx, ob) in enumerate(outs):
+        g = info["group_of"][b]
+        pl = int(info["prompt_len"][g])
+        for i, j in enumerate(idx.tolist()):
+            if i >= pl or b == info["rep"][g]:
+                out_rows[j] = ob[i]
+    return torch.stack(out_rows) if T else o
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_matches_library_sdpa(name):
+    info, x = _setup(SMALL[name], permute=True)
+    scale = 1.0 / math.sqrt(SMALL[name].head_dim)
+    o, lse = oracle.split_attention_forward(x.q, x.k, x.v, info)
+    ref = _sdpa_packed(*(torch.from_numpy(a.astype(np.float64)) for a in (x.q, x.k, x.v)), info, scale)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_backward_matches_autograd(name):
+    info, x = _setup(SMALL[name], permute=True)
+    scale = 1.0 / math.sqrt(SMALL[name].head_dim)
+    q, k, v = (torch.from_numpy(a.astype(np.float64)).requires_grad_() for a in (x.q, x.k, x.v))
+    out = _sdpa_packed(q, k, v, info, scale)
+    (out * torch.from_numpy(x.do.astype(np.float64))).sum().backward()
+    dq, dk, dv = oracle.split_attention_backward(x.q, x.k, x.v, x.do, info)
+    for got, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-11)
+
+
+def test_single_response_is_plain_causal():
+    w = SMALL["mha"].scaled(num_prompts=1, rollout_n=1, seed=9)
+    info, x = _setup(w)
+    o, lse = oracle.split_attention_forward(x.q, x.k, x.v, info)
+    Q, K, V = (torch.from_numpy(a.astype(np.float64)).transpose(0, 1) for a in (x.q, x.k, x.v))
+    ref = F.scaled_dot_product_attention(Q, K, V, is_causal=True).transpose(0, 1)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12, rtol=0)
+    # the log-sum-exp, by direct definition on the same single sequence
+    s = (Q @ K.transpose(1, 2)) / math.sqrt(w.head_dim)
+    s = s.masked_fill(torch.triu(torch.ones(info["T"], info["T"], dtype=torch.bool), 1), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, -1).numpy(), atol=1e-12, rtol=0)
+
+
+def test_empty_responses_reduce_to_prompt_attention():
+    w = SMALL["mha"].scaled(num_prompts=1, rollout_n=2, resp_len_range=(0, 0), seed=10)
+    info, x = _setup(w)
+    assert info["T"] == w.prompt_len
+    o, _ = oracle.split_attention_forward(x.q, x.k, x.v, info)
+    Q, K, V = (torch.from_numpy(a.astype(np.float64)).transpose(0, 1) for a in (x.q, x.k, x.v))
+    ref = F.scaled_dot_product_attention(Q, K, V, is_causal=True).transpose(0, 1)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12, rtol=0)
+
+
+def test_closed_forms():
+    w = SMALL["gqa_ragged_unpad"]
+    info, x = _setup(w)
+    x.v = x.v.astype(np.float64)
+    T, Hq, d = x.q.shape
+    # constant V rows -> every output is that constant
+    v_const = np.broadcast_to(np.linspace(-1, 1, d), x.v.shape).copy()
+    o, _ = oracle.split_attention_forward(x.q, x.k, v_const, info)
+    np.testing.assert_allclose(o, np.broadcast_to(np.linspace(-1, 1, d), o.shape), atol=1e-13)
+    # Q = 0 -> uniform softmax: output is the mean of the visible V rows, LSE = log(#visible)
+    o, lse = oracle.split_attention_forward(np.zeros_like(x.q), x.k, x.v, info)
+    ratio = Hq // x.k.shape[1]
+    for g in range(info["G"]):
+        po, pl = info["prompt_off"][g], info["prompt_len"][g]
+        for i in range(pl):            # prompt row i: prefix mean of its own prompt
+            vis = np.arange(po, po + i + 1)
+            for h in range(Hq):
+                np.testing.assert_allclose(o[po + i, h], x.v[vis, h // ratio].mean(0), atol=1e-13)
+                assert abs(lse[h, po + i] - math.log(len(vis))) < 1e-13
+        for b in info["groups"][g]:
+            ro, rl = info["resp_off"][b], info["resp_len"][b]
+            for i in range(rl):        # response row i: all prompt keys plus own keys 0..i
+                vis = np.concatenate([np.arange(po, po + pl), np.arange(ro, ro + i + 1)])
+                for h in range(Hq):
+                    np.testing.assert_allclose(o[ro + i, h], x.v[vis, h // ratio].mean(0), atol=1e-13)
+                    assert abs(lse[h, ro + i] - math.log(len(vis))) < 1e-13
+    # first prompt row sees only itself
+    o, _ = oracle.split_attention_forward(x.q, x.k, x.v, info)
+    for g in range(info["G"]):
+        po = info["prompt_off"][g]
+        for h in range(Hq):
+            np.testing.assert_allclose(o[po, h], x.v[po, h // ratio], atol=1e-14)
+
+
+def test_finite_differences():
+    w = WORKLOADS["tiny_fp32"].scaled(prompt_len=12, response_len=5, head_dim=8, seed=11)
+    info, x = _setup(w, permute=True)
+    rng = np.random.default_rng(3)
+    q, k, v, do = (a.astype(np.float64) for a in (x.q, x.k, x.v, x.do))
+    dq, dk, dv = oracle.split_attention_backward(q, k, v, do, info)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.split_attention_forward(q_, k_, v_, info)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for _ in range(3):
+        eq, ek, ev = (rng.standard_normal(a.shape) for a in (q, k, v))
+        fd = (loss(q + h * eq, k + h * ek, v + h * ev) - loss(q - h * eq, k - h * ek, v - h * ev)) / (2 * h)
+        an = (dq * eq).sum() + (dk * ek).sum() + (dv * ev).sum()
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (fd, an)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa_ragged_unpad"])
+def test_gradient_invariants(name):
+    info, x = _setup(SMALL[name], permute=True)
+    dq, dk, dv = oracle.split_attention_backward(x.q, x.k, x.v, x.do, info)
+    Hq, Hkv = x.q.shape[1], x.k.shape[1]
+    ratio = Hq // Hkv
+    do = x.do.astype(np.float64)
+    for j in range(Hkv):
+        # softmax rows sum to 1: the values' gradient sums to the output gradient
+        np.testing.assert_allclose(dv[:, j].sum(0), do[:, j * ratio:(j + 1) * ratio].sum((0, 1)),
+                                   atol=1e-11)
+        # rows of dS sum to 0: the keys' gradient sums to 0
+        np.testing.assert_allclose(dk[:, j].sum(0), 0.0, atol=1e-11)
+
+
+def test_sampled_rows_match_full():
+    w = SMALL["gqa_ragged_unpad"]
+    info, x = _setup(w, permute=True)
+    o, lse = oracle.split_attention_forward(x.q, x.k, x.v, info)
+    dq, dk, dv = oracle.split_attention_backward(x.q, x.k, x.v, x.do, info)
+    rows = np.random.default_rng(1).choice(info["T"], 12, replace=False)
+    heads = [0, 3]
+    o_s, lse_s = oracle.forward_rows(x.q, x.k, x.v, info, rows, heads)
+    np.testing.assert_allclose(o_s, o[rows][:, heads], atol=1e-13)
+    np.testing.assert_allclose(lse_s, lse[heads][:, rows].T, atol=1e-13)
+    dq_s = oracle.dq_rows(x.q, x.k, x.v, x.do, info, rows, heads)
+    np.testing.assert_allclose(dq_s, dq[rows][:, heads], atol=1e-12)
+    dk_s, dv_s = oracle.dkdv_rows(x.q, x.k, x.v, x.do, info, rows, [0, 1])
+    np.testing.assert_allclose(dk_s, dk[rows], atol=1e-12)
+    np.testing.assert_allclose(dv_s, dv[rows], atol=1e-12)
+
+
+def test_attended_pairs_brute_force():
+    for name in SMALL:
+        info, _ = _setup(SMALL[name], permute=True)
+        pairs = set()
+        plain = 0
+        for b in range(info["B"]):
+            idx = oracle.sample_rows(info, b)
+            plain += len(idx) * (len(idx) + 1) // 2
+            for i in range(len(idx)):
+                for kk in range(i + 1):
+                    pairs.add((int(idx[i]), int(idx[kk])))
+        assert oracle.attended_pairs(info) == (len(pairs), plain)
+
+
+# --- planted mistakes: each must be caught by one of the pins above -------------------------
+
+def _planted_causal_block_off_by_one(Qs, Ks, Vs, i0, i1, scale, dOs=None):
+    s = scale * (Qs[i0:i1] @ Ks[:i1].T)
+    future = np.arange(i1)[None, :] >= np.arange(i0, i1)[:, None]   # drops the diagonal key
+    future[:, 0] = False
+    s[future] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    o = p @ Vs[:i1]
+    lse = (m + np.log(l))[:, 0]
+    if dOs is None:
+        return p, o, lse, None
+    dO = dOs[i0:i1]
+    dS = p * (dO @ Vs[:i1].T - (dO * o).sum(axis=1, keepdims=True))
+    return p, o, lse, dS
+
+
+def test_planted_mask_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(oatt, "_causal_block", _planted_causal_block_off_by_one)
+    with pytest.raises(AssertionError):
+        test_forward_matches_library_sdpa("tiny")
+
+
+def test_planted_gqa_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(oatt, "_kv_head", lambda h, Hq, Hkv: h % Hkv)
+    with pytest.raises(AssertionError):
+        test_forward_matches_library_sdpa("gqa_ragged_unpad")
+
+
+def test_planted_sibling_leak_is_caught(monkeypatch):
+    """A response that also saw its siblings' rows must fail the pins."""
+    real = oracle.dedup.sample_rows
+
+    def leaky(info, b):
+        g = info["group_of"][b]
+        first = info["groups"][g][0]
+        idx = real(info, b)
+        if b != first:
+            extra = real(info, first)[info["prompt_len"][g]:]
+            pl = info["prompt_len"][g]
+            idx = np.concatenate([idx[:pl], extra, idx[pl:]])
+        return idx
+
+    monkeypatch.setattr(oatt, "sample_rows", leaky)
+    with pytest.raises(AssertionError):
+        test_closed_forms()
+
+
+def test_planted_prompt_grad_mistake_is_caught(monkeypatch):
+    """Counting prompt rows' dO once per member (not once) must fail the autograd pin."""
+    real = oatt.split_attention_backward
+
+    def doubled(q, k, v, dout, info, scale=None):
+        q_, k_, v_, T, Hq, Hkv, d, scale = oatt._prep(q, k, v, scale)
+        dq = np.zeros_like(q_)
+        dk = np.zeros_like(k_)
+        dv = np.zeros_like(v_)
+        for b in range(info["B"]):
+            idx = oracle.sample_rows(info, b)
+            for h in range(Hq):
+                j = h // (Hq // Hkv)
+                L = len(idx)
+                p, _, _, dS = oatt._causal_block(q_[idx, h], k_[idx, j], v_[idx, j], 0, L, scale,
+                                                 np.asarray(dout, np.float64)[idx, h])
+                dv[idx, j] += p.T @ np.asarray(dout, np.float64)[idx, h]
+                dq[idx, h] += scale * dS @ k_[idx, j]
+                dk[idx, j] += scale * dS.T @ q_[idx, h]
+        return dq, dk, dv
+
+    monkeypatch.setattr(oracle, "split_attention_backward", doubled)
+    with pytest.raises(AssertionError):
+        test_backward_matches_autograd("tiny")
+    assert real is not doubled

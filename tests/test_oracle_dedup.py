@@ -1,0 +1,207 @@
+"""Pins for the oracle's grouping, packing and reconstruction (CPU only).
+
+Each check ties the oracle to something other than itself: the pages'
+worked examples (tests/golden/), brute force with an independent
+equivalence-class construction, token arithmetic, and round trips.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import WORKLOADS, make_batch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _classes_by_dict(ids, P):
+    """Independent grouping: bucket rows by the tuple of their prompt tokens,
+    order buckets by their smallest member."""
+    buckets = {}
+    for b in range(ids.shape[0]):
+        buckets.setdefault(tuple(ids[b, :P].tolist()), []).append(b)
+    return sorted(buckets.values(), key=lambda m: m[0])
+
+
+def test_page_grouping_example():
+    g = _golden("find_prompt_groups_example.json")
+    rng = np.random.default_rng(0)
+    P, R = 6, 3
+    prompts = rng.integers(0, 50, size=(2, P))
+    ids = np.concatenate([prompts[g["prompt_of_sample"]], rng.integers(0, 50, size=(g["batch"], R))], 1)
+    groups, uniq = oracle.find_prompt_groups(ids, R)
+    assert groups == g["prompt_groups"]
+    assert uniq.shape == (2, P)
+    np.testing.assert_array_equal(uniq, prompts)
+
+
+@pytest.mark.parametrize("B,P", [(1, 1), (3, 2), (4, 2), (5, 2), (6, 2), (4, 3)])
+def test_grouping_exhaustive_binary(B, P):
+    """Every batch of B rows over the vocabulary {0, 1} with prompt length P."""
+    R = 1
+    for bits in itertools.product([0, 1], repeat=B * P):
+        prm = np.array(bits, dtype=np.int64).reshape(B, P)
+        ids = np.concatenate([prm, np.arange(B)[:, None] % 2], 1)
+        groups, uniq = oracle.find_prompt_groups(ids, R)
+        assert groups == _classes_by_dict(ids, P)
+        for g, m in enumerate(groups):
+            np.testing.assert_array_equal(uniq[g], prm[m[0]])
+
+
+def test_grouping_adversarial():
+    P, R = 8, 4
+    base = np.arange(P) + 10
+    rows = [base.copy() for _ in range(7)]
+    rows[1][0] += 1          # differs only in the first prompt token
+    rows[2][-1] += 1         # differs only in the last prompt token
+    rows[4] = rows[1].copy()  # interleaved member of row 1's group
+    ids = np.stack([np.concatenate([r, np.full(R, i)]) for i, r in enumerate(rows)])
+    groups, _ = oracle.find_prompt_groups(ids, R)
+    # rows 0,3,5,6 share the base prompt (their responses differ); 1 and 4 share one; 2 alone
+    assert groups == [[0, 3, 5, 6], [1, 4], [2]]
+    # a response token equal to a prompt token never matters
+    groups_all_resp, _ = oracle.find_prompt_groups(ids, 0)
+    assert groups_all_resp == [[i] for i in range(7)]
+    # response_length == seq_len: empty prompts, one group
+    groups_empty, uniq = oracle.find_prompt_groups(ids, P + R)
+    assert groups_empty == [list(range(7))] and uniq.shape == (1, 0)
+
+
+def test_concatenation_order_example():
+    g = _golden("concatenation_example.json")
+    tok = {"A": [1, 2, 3], "B": [4, 5, 6], "R1": [11, 12], "R2": [21, 22], "R3": [31, 32], "R4": [41, 42]}
+    ids = np.array([tok[p] + tok[r] for p, r in g["samples"]], dtype=np.int64)
+    pos = np.tile(np.arange(ids.shape[1]), (ids.shape[0], 1))
+    groups, uniq = oracle.find_prompt_groups(ids, 2)
+    assert groups == [[0, 1], [2, 3]]
+    dids, dpos, info = oracle.create_deduplicated_batch(ids, pos, 2, groups, uniq)
+    expect = sum((tok[x] for x in g["packed"]), [])
+    assert dids.shape == (1, len(expect))
+    assert dids[0].tolist() == expect
+    # positions are gathered: prompt 0..2, each response 3..4
+    assert dpos[0].tolist() == [0, 1, 2, 3, 4, 3, 4, 0, 1, 2, 3, 4, 3, 4]
+
+
+def test_redundancy_example_arithmetic():
+    g = _golden("redundancy_example.json")
+    P, n, R = g["prompt_len"], g["num_responses"], g["response_len"]
+    ids = np.zeros((n, P + R), dtype=np.int64)
+    ids[:, P:] = np.arange(n)[:, None]
+    pos = np.tile(np.arange(P + R), (n, 1))
+    groups, uniq = oracle.find_prompt_groups(ids, R)
+    _, _, info = oracle.create_deduplicated_batch(ids, pos, R, groups, uniq)
+    total, unique, red = oracle.redundancy_counts(info)
+    assert total == g["total_tokens"]
+    assert unique == g["unique_tokens"]
+    assert round(100 * red) == g["redundancy_percent_rounded"]
+
+
+def test_redundancy_workload_tokens():
+    """The 10240/1024 workload: 110Ki total, 20Ki unique, 82% redundant."""
+    w = WORKLOADS["redundancy_1x10_p10240_r1024"]
+    bt = make_batch(w)
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length,
+                                                  groups, uniq)
+    total, unique, red = oracle.redundancy_counts(info)
+    assert (total, unique) == (112640, 20480)
+    assert round(100 * red) == 82
+
+
+def _check_plan(ids, pos, mask, R, use_unpad, groups, uniq):
+    dids, dpos, info = oracle.create_deduplicated_batch(ids, pos, R, groups, uniq,
+                                                        attention_mask=mask, use_unpad=use_unpad)
+    B, S = ids.shape
+    P = S - R
+    keep = (mask != 0) if use_unpad else np.ones_like(ids, dtype=bool)
+    # token count: each group's first-member prompt once plus every kept response token
+    T = sum(int(keep[m[0], :P].sum()) for m in groups) + int(keep[:, P:].sum())
+    assert info["T"] == T == dids.shape[1]
+    flat_ids, flat_pos = ids.reshape(-1), pos.reshape(-1)
+    np.testing.assert_array_equal(dids[0], flat_ids[info["src"]])
+    np.testing.assert_array_equal(dpos[0], flat_pos[info["src"]])
+    # segments tile [0, T) in the concatenation order
+    cursor = 0
+    for g, m in enumerate(groups):
+        assert info["prompt_off"][g] == cursor
+        cursor += info["prompt_len"][g]
+        for b in m:
+            assert info["resp_off"][b] == cursor
+            cursor += info["resp_len"][b]
+    assert cursor == T
+    # dst inverts src on the rows that were packed; prompt copies map to the first member's rows
+    for j, s in enumerate(info["src"]):
+        assert info["dst"][s] == j
+    for b in range(B):
+        g = info["group_of"][b]
+        r = groups[g][0]
+        for t in range(S):
+            j = info["dst"][b * S + t]
+            if t < P:
+                assert j == info["dst"][r * S + t]
+                assert (j >= 0) == bool(keep[r, t])
+            else:
+                assert (j >= 0) == bool(keep[b, t])
+    return info
+
+
+@pytest.mark.parametrize("use_unpad", [False, True])
+@pytest.mark.parametrize("permute", [False, True])
+def test_pack_tiny_workload(use_unpad, permute):
+    w = WORKLOADS["tiny_fp32"]
+    if use_unpad:
+        w = w.scaled(resp_len_range=(0, 32))
+    bt = make_batch(w, permute=permute)
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    assert groups == _classes_by_dict(bt.input_ids, w.prompt_len)
+    _check_plan(bt.input_ids, bt.position_ids, bt.attention_mask, bt.response_length, use_unpad,
+                groups, uniq)
+
+
+def test_pack_unpad_prompt_padding():
+    """Left-padded prompts: masked prompt tokens are dropped for the whole group."""
+    rng = np.random.default_rng(5)
+    B, P, R = 6, 10, 5
+    ids = rng.integers(1, 9, size=(B, P + R))
+    ids[:3, :P] = ids[0, :P]
+    ids[3:, :P] = ids[0, :P] + 10   # a second, different prompt
+    mask = np.ones_like(ids)
+    mask[:3, :4] = 0      # left pads on group 0's prompt
+    mask[1, P + 2:] = 0    # short response
+    mask[4, P:] = 0        # all-pad response
+    pos = np.cumsum(mask, 1) - 1
+    groups, uniq = oracle.find_prompt_groups(ids, R)
+    info = _check_plan(ids, pos, mask, R, True, groups, uniq)
+    assert info["prompt_len"].tolist() == [6, 10]
+    assert info["resp_len"].tolist() == [5, 2, 5, 5, 0, 5]
+
+
+def test_reconstruct_round_trip():
+    rng = np.random.default_rng(7)
+    w = WORKLOADS["tiny_fp32"].scaled(resp_len_range=(0, 32))
+    bt = make_batch(w, permute=True)
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length,
+                                                  groups, uniq, attention_mask=bt.attention_mask,
+                                                  use_unpad=True)
+    B, S, W = w.batch, w.seq_len, 5
+    X = rng.standard_normal((B, S, W))
+    P = w.prompt_len
+    for m in groups:      # prompt rows identical within a group, as for real hidden states
+        X[m, :P] = X[m[0], :P]
+    packed = oracle.pack_rows(X, info)
+    assert packed.shape == (info["T"], W)
+    Y = oracle.reconstruct_sequences(packed[None], info)
+    keep = bt.attention_mask != 0
+    np.testing.assert_array_equal(Y[keep], X[keep])
+    assert not Y[~keep].any()
+    # 2-D input is accepted too and gives the same
+    np.testing.assert_array_equal(oracle.reconstruct_sequences(packed, info), Y)
