@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Throughput of prompt-deduplicated split attention on one MI355X.
+
+One step is one pass of the whole hot path over one synthetic batch already
+resident in HBM:
+  group (spd_group) -> pack ids/positions (spd_pack) -> pack the per-token
+  rows entering the layer (spd_pack_rows) -> split-attention forward
+  (spd_split_attn_fwd) -> backward (spd_split_attn_bwd) -> reconstruct the
+  attention output to [batch, seq, Hq*d] (spd_reconstruct).
+
+`value` is the useful split-attention forward+backward work per step
+(4*d*Hq FLOP per attended (query, key) pair forward, 10*d*Hq backward,
+pairs counted from the plan) divided by the measured time of the whole step.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "split-attn fwd+bwd TFLOP/s & % bf16 MFMA peak; pack/reconstruct GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def attended_pairs(info):
+    """(query, key) pairs split attention evaluates, from the plan's segment lengths."""
+    G = info["G"]
+    pl = info["prompt_len"][:G].cpu().tolist()
+    rl = info["resp_len"].cpu().tolist()
+    gof = info["group_of"].cpu().tolist()
+    pairs = sum(p * (p + 1) // 2 for p in pl)
+    for b, r in enumerate(rl):
+        pairs += r * pl[gof[b]] + r * (r + 1) // 2
+    return pairs
+
+
+def cpu_baseline(w, bt, pairs_per_head, budget_heads=1):
+    """The oracle, as it stands, on one query head of the same workload (fwd + bwd, fp64)."""
+    import numpy as np
+
+    import oracle
+    from workloads import make_attn_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"],
+                           default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
+                                                  attention_mask=bt.attention_mask, use_unpad=w.use_unpad)
+    x = make_attn_inputs(w, info["T"])
+    heads = list(range(budget_heads))
+    t0 = time.perf_counter()
+    oracle.split_attention_forward(x.q, x.k, x.v, info, heads=heads)
+    oracle.split_attention_backward(x.q, x.k, x.v, x.do, info, heads=heads)
+    dt = time.perf_counter() - t0
+    flops = 14 * w.head_dim * len(heads) * pairs_per_head
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle (non-deduplicated per-sample attention), forward+backward of "
+                      f"{len(heads)} of {w.num_q_heads} query heads over the full batch; {dt:.1f} s; "
+                      f"useful FLOPs counted as on the GPU; host cores available "
+                      f"{len(os.sched_getaffinity(0))}, {platform.processor() or platform.machine()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None, help="workload name in workloads.WORKLOADS")
+    ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    ap.add_argument("--profile-steps", type=int, default=5, help="steps timed per kernel with HIP events")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "groups shard across GPUs without exchange, so the per-GPU figure is the one reported.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import shared_prompt_dedup_amd as spd
+    from workloads import BENCH_WORKLOAD, WORKLOADS, make_attn_inputs, make_batch
+
+    name = args.workload or BENCH_WORKLOAD
+    w = WORKLOADS[name]
+    assert w.dtype == "bf16"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bt = make_batch(w)
+    ids = torch.from_numpy(bt.input_ids).to(dev)
+    pos = torch.from_numpy(bt.position_ids).to(dev)
+    mask = torch.from_numpy(bt.attention_mask).to(dev)
+    R = bt.response_length
+    B, S = ids.shape
+    Hq, Hkv, d = w.num_q_heads, w.num_kv_heads, w.head_dim
+    W = Hq * d
+
+    groups, uniq = spd.group(ids, R, return_lists=False)
+    _, _, info = spd.pack(ids, pos, R, groups, uniq, attention_mask=mask, use_unpad=w.use_unpad)
+    T = info["T"]
+    pairs = attended_pairs(info)
+    x = make_attn_inputs(w, T)
+    conv = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, dout = conv(x.q_bits), conv(x.k_bits), conv(x.v_bits), conv(x.do_bits)
+    del x
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    hidden = torch.randn((B, S, W), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    def step():
+        g, u = spd.group(ids, R, return_lists=False)
+        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=w.use_unpad)
+        packed = spd.pack_rows(hidden, inf)
+        o, lse = spd.split_attn_fwd(q, k, v, inf)
+        dq, dk, dv = spd.split_attn_bwd(q, k, v, o, lse, dout, inf)
+        out = spd.reconstruct(o.view(T, W), inf)
+        return packed, out, dq, dk, dv
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    fwd_flops = 4 * d * Hq * pairs
+    bwd_flops = 10 * d * Hq * pairs
+    value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+
+    # Per-kernel HIP events (recorded by the library on the launch stream).
+    spd.profile_begin()
+    for _ in range(args.profile_steps):
+        step()
+    torch.cuda.synchronize()
+    prof = spd.profile_end()
+    kern_ms = {kname: (tot / n if n else None) for kname, (n, tot) in prof.items()}
+    row_bytes = W * 2
+    kernel_work = {
+        "fwd": ("mfma", 4 * d * Hq * pairs),
+        "bwd_dkdv": ("mfma", 8 * d * Hq * pairs),      # S, dP recomputed; dV, dK
+        "bwd_dq": ("mfma", 6 * d * Hq * pairs),        # S, dP recomputed; dQ
+        "bwd_pre": ("hbm", 2 * T * W * 2 + T * Hq * 4),
+        "reconstruct": ("hbm", T * row_bytes + B * S * row_bytes),
+        "pack_rows": ("hbm", 2 * T * row_bytes),
+    }
+    kernels = {}
+    for kname, (bound, work) in kernel_work.items():
+        ms = kern_ms.get(kname)
+        if not ms:
+            continue
+        if bound == "mfma":
+            ach = work / (ms * 1e-3) / 1e12
+            kernels[kname] = {"ms": round(ms, 4), "bound": "mfma", "achieved": round(ach, 2),
+                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = work / (ms * 1e-3) / 1e9
+            kernels[kname] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    dom = max(kernels, key=lambda kk: kernels[kk]["ms"])
+    roof = dict(kernels[dom])
+    roof.pop("ms")
+    roof = {"kernel": dom, **roof, "traffic": None}
+
+    attn_ms = sum(kern_ms[kk] for kk in ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv") if kern_ms.get(kk))
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "unique_prompts": w.num_prompts, "prompt_len": w.prompt_len,
+                   "response_len": w.response_len, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "packed_tokens": T, "attended_pairs": pairs, "parallelism": "single GPU"},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "attention_kernels_tflops": round((fwd_flops + bwd_flops) / (attn_ms * 1e-3) / 1e12, 2),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if args.cpu_baseline == "on":
+        result["cpu_baseline"] = cpu_baseline(w, bt, pairs)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

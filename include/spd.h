@@ -1,0 +1,240 @@
+/*
+ * spd.h -- C ABI of the prompt-deduplicated split-attention library (libspd.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "How Prompt Deduplication Works":
+ *   spd_group            -- Core Algorithm, "Finding Prompt Groups"
+ *   spd_pack             -- Core Algorithm, "Creating Deduplicated Batch";
+ *                           "Working with Packed/Unpacked Sequences"
+ *   spd_pack_rows        -- the same packing applied to per-token rows
+ *   spd_split_attn_fwd   -- Phase 2, "Split Attention Optimization"
+ *   spd_split_attn_bwd   -- "Correctness & Gradients" (gradients flow through
+ *                           the deduplicated computation)
+ *   spd_reconstruct      -- Core Algorithm, "Reconstructing Original Batch";
+ *                           Phase 3, "Transparent Reconstruction"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named as device pointers must be device memory of the current
+ *   HIP device, 16-byte aligned, contiguous, row-major.  The library never
+ *   allocates, frees or keeps a pointer after the call returns: the caller
+ *   owns every buffer, including workspaces sized by the *_workspace_bytes
+ *   queries.
+ * - Every call is asynchronous on the given stream (a hipStream_t passed as
+ *   void*; NULL = the null stream) and keeps no state between calls (apart
+ *   from the opt-in, per-thread kernel timing at the end of this header), so
+ *   calls on different streams may run concurrently on disjoint buffers.
+ * - Arguments are validated on the host before anything is launched; a
+ *   non-zero spd_status is returned and nothing runs.  SPD_ERR_HIP means a
+ *   launch failed (hipGetLastError after the launch); spd_last_hip_error()
+ *   gives the HIP code.
+ * - Index arrays are int32 (packed rows, batch rows and (b*S+t) indices all
+ *   stay below 2^31); byte offsets inside kernels are 64-bit.
+ *
+ * Notation: B samples, S padded sequence length, P = S - response_length
+ * prompt columns, G groups, T packed tokens, Hq / Hkv query / key-value heads,
+ * d head dimension.
+ */
+#ifndef SPD_H
+#define SPD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spd_status {
+  SPD_OK = 0,
+  SPD_ERR_INVALID_ARG = -1, /* null pointer, negative or inconsistent size */
+  SPD_ERR_UNSUPPORTED = -2, /* a shape or dtype this build does not handle */
+  SPD_ERR_ALIGNMENT = -3,   /* pointer or row size not a multiple of 16 bytes */
+  SPD_ERR_WORKSPACE = -4,   /* workspace null or smaller than the query says */
+  SPD_ERR_HIP = -5          /* a HIP launch failed */
+} spd_status;
+
+typedef enum spd_dtype { SPD_F32 = 0, SPD_BF16 = 1 } spd_dtype;
+
+/*
+ * The deduplication plan: device arrays owned by the caller, filled by
+ * spd_group (group arrays) and spd_pack (segment arrays).  Capacities depend
+ * only on B and S, so everything can be allocated before the number of groups
+ * G or packed tokens T is known.  counts[0] = G and counts[1] = T are written
+ * on the device; the caller reads them back when it needs host copies.
+ *
+ * Segments: group g's prompt occupies packed rows
+ * [prompt_off[g], prompt_off[g] + prompt_len[g]); its members' responses
+ * follow in ascending sample order, sample b at [resp_off[b], resp_off[b] +
+ * resp_len[b]).  seg_start[j] is the first row of the segment containing j.
+ */
+typedef struct spd_plan {
+  int64_t B;            /* host: samples */
+  int64_t S;            /* host: padded sequence length */
+  int64_t P;            /* host: prompt columns, S - response_length */
+  int32_t *group_of;    /* [B]     group of each sample */
+  int32_t *grp_off;     /* [B + 1] CSR offsets of groups (first G + 1 used) */
+  int32_t *grp_idx;     /* [B]     members, grouped, ascending within a group */
+  int32_t *rep;         /* [B]     first member of each group (first G used) */
+  int32_t *prompt_off;  /* [B]     packed start of each group's prompt */
+  int32_t *prompt_len;  /* [B]     packed prompt tokens of each group */
+  int32_t *resp_off;    /* [B]     packed start of each sample's response */
+  int32_t *resp_len;    /* [B]     packed response tokens of each sample */
+  int32_t *src;         /* [B * S] capacity; packed row j -> b * S + t (first T used) */
+  int32_t *dst;         /* [B * S] (b, t) -> packed row, or -1 if no packed token maps */
+  int32_t *seg_start;   /* [B * S] capacity; first packed row of j's segment */
+  int32_t *counts;      /* [4]     counts[0] = G, counts[1] = T, [2..3] reserved */
+} spd_plan;
+
+/* ---------------------------------------------------------------- grouping */
+
+/* Workspace bytes spd_group needs for a batch of B rows of S tokens. */
+size_t spd_group_workspace_bytes(int64_t B, int64_t S);
+
+/*
+ * Group samples by identical prompt ("Finding Prompt Groups").
+ *   input_ids        device int64 [B, S].
+ *   response_length  the response columns; the prompt is the first
+ *                    P = S - response_length columns of every row
+ *                    (0 <= response_length <= S; plan->P must equal P).
+ *   plan             writes group_of, grp_off, grp_idx, rep, counts[0] = G.
+ *                    Groups are numbered in order of first occurrence and list
+ *                    their members ascending; two rows group together exactly
+ *                    when all P prompt ids are equal (a hash narrows the
+ *                    candidates, a full comparison decides).
+ *   unique_prompts   optional (NULL to skip) device int64 with capacity
+ *                    [B, P]; row g < G receives group g's prompt ids.
+ * Constraints: 1 <= B <= 65536, B * S < 2^31.
+ */
+spd_status spd_group(const int64_t *input_ids, int64_t B, int64_t S, int64_t response_length,
+                     const spd_plan *plan, int64_t *unique_prompts,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------------- packing */
+
+/* Workspace bytes spd_pack needs. */
+size_t spd_pack_workspace_bytes(int64_t B, int64_t S);
+
+/*
+ * Build the packed sequence ("Creating Deduplicated Batch"), after spd_group
+ * on the same plan.  Order: [prompt of group 0][responses of its members,
+ * ascending][prompt of group 1]...  The prompt copy packed for a group, and
+ * its positions and mask, are its first member's.
+ *   input_ids, position_ids  device int64 [B, S]; positions are gathered,
+ *                            not renumbered.
+ *   attention_mask           device [B, S] of mask_elem_bytes-byte integers
+ *                            (1, 4 or 8), non-zero = valid; may be NULL when
+ *                            use_unpad == 0 (padded mode keeps every token).
+ *   use_unpad                1: drop tokens whose mask is 0 ("Unpacked
+ *                            Format"); 0: keep every token.
+ *   dedup_ids, dedup_pos     device int64 with capacity B * S; the first T
+ *                            entries receive the packed ids and positions.
+ * Writes prompt_off, prompt_len, resp_off, resp_len, src, dst, seg_start and
+ * counts[1] = T.
+ */
+spd_status spd_pack(const int64_t *input_ids, const int64_t *position_ids,
+                    const void *attention_mask, int32_t mask_elem_bytes, int32_t use_unpad,
+                    const spd_plan *plan, int64_t *dedup_ids, int64_t *dedup_pos,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Pack per-token rows with the plan: packed[j, :] = rows[src[j], :].
+ *   rows       device [B, S, row_bytes] (any element type; copied as bytes).
+ *   packed     device [T, row_bytes].
+ *   T          the packed length (counts[1] of the plan).
+ * row_bytes must be a positive multiple of 16.
+ */
+spd_status spd_pack_rows(const spd_plan *plan, int64_t T, const void *rows, int64_t row_bytes,
+                         void *packed, void *stream);
+
+/*
+ * Reconstruct the batch ("Reconstructing Original Batch"):
+ * out[b, t, :] = packed[dst[b * S + t], :], or zeros where dst is -1.  Each
+ * packed prompt row is read once and written to every member of its group.
+ *   packed     device [T, row_bytes].
+ *   out        device [B, S, row_bytes].
+ * row_bytes must be a positive multiple of 16.
+ */
+spd_status spd_reconstruct(const spd_plan *plan, int64_t T, const void *packed, int64_t row_bytes,
+                           void *out, void *stream);
+
+/* ---------------------------------------------------------- split attention */
+
+typedef struct spd_attn_desc {
+  int32_t num_q_heads;   /* Hq */
+  int32_t num_kv_heads;  /* Hkv; Hq % Hkv == 0, query head h reads kv head h / (Hq / Hkv) */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t dtype;         /* spd_dtype of q, k, v, o, dout, dq, dk, dv */
+  float softmax_scale;   /* usually 1 / sqrt(d); must be > 0 */
+} spd_attn_desc;
+
+/* Workspace bytes the attention calls need for T packed rows of a B-sample plan. */
+size_t spd_attn_workspace_bytes(const spd_attn_desc *desc, int64_t B, int64_t T);
+
+/*
+ * Split attention forward ("Split Attention Optimization").  In the packed
+ * batch, a prompt row i of group g attends causally to its prompt's rows
+ * 0..i; a response row i of sample b attends to all of its group's prompt
+ * rows and to its own response rows 0..i, never to another group or a
+ * sibling response.  This equals causal attention over each sample's own
+ * [prompt][response] sequence.
+ *   q        device [T, Hq, d];  k, v  device [T, Hkv, d]  (dtype of desc)
+ *   o        device [T, Hq, d]   softmax(scale q k^T) v, same dtype
+ *   lse      device float [Hq, T]  natural-log softmax denominator per row,
+ *            kept for the backward
+ *   T        the packed length written by spd_pack (rows >= T are never read)
+ * bf16 runs on matrix cores with fp32 accumulation and one rounding of o;
+ * fp32 is a plain-arithmetic path for small problems.
+ */
+spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T,
+                              const void *q, const void *k, const void *v, void *o, float *lse,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Split attention backward ("Correctness & Gradients").  Given o and lse from
+ * the forward and dout = dL/do, writes dq [T, Hq, d], dk, dv [T, Hkv, d].
+ * A prompt key's dk / dv sum over the prompt's own causal queries and every
+ * response row of its group; query heads sharing a kv head add into it.
+ * Accumulation is fp32 and each output is rounded once.  No atomics: results
+ * are bitwise reproducible run to run.
+ */
+spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T,
+                              const void *q, const void *k, const void *v, const void *o,
+                              const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------ kernel timing */
+
+/*
+ * Opt-in timing of the library's main kernels with HIP events recorded on the
+ * stream each kernel is launched on (for benchmarks; per host thread).
+ * Between spd_profile_begin() and spd_profile_end() every entry point records
+ * an event pair around each of its main kernels, at most 1024 launches per
+ * kernel.  spd_profile_end() waits for those events, writes per kernel id the
+ * number of timed launches and their summed milliseconds into arrays of
+ * SPD_K_COUNT entries, and stops recording.  When no profile is active the
+ * entry points record nothing.
+ */
+enum {
+  SPD_K_FWD = 0,          /* split-attention forward kernel */
+  SPD_K_BWD_PRE = 1,      /* backward: rowsum(dO * O) */
+  SPD_K_BWD_DQ = 2,       /* backward: dq kernel */
+  SPD_K_BWD_DKDV = 3,     /* backward: dk / dv kernel */
+  SPD_K_RECONSTRUCT = 4,  /* reconstruct gather (and the zero fill) */
+  SPD_K_PACK_ROWS = 5,    /* row packing gather */
+  SPD_K_COUNT = 6
+};
+spd_status spd_profile_begin(void);
+spd_status spd_profile_end(int64_t *launches, double *total_ms);
+
+/* ------------------------------------------------------------------- misc */
+
+const char *spd_status_string(spd_status status);
+int spd_last_hip_error(void);   /* HIP error code behind the last SPD_ERR_HIP on this thread */
+int spd_version(void);          /* major * 10000 + minor * 100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPD_H */

@@ -129,15 +129,17 @@ def split_attention_forward(q, k, v, info, scale=None, heads=None):
     return o, lse
 
 
-def split_attention_backward(q, k, v, dout, info, scale=None):
+def split_attention_backward(q, k, v, dout, info, scale=None, heads=None):
     """Gradients ``(dq, dk, dv)`` of the packed split-attention output.
 
     Per sample: textbook causal-attention backward with that sample's
     ``dO`` (see the module docstring), then scatter-add onto packed rows;
-    query heads sharing a kv head add into it.
+    query heads sharing a kv head add into it.  ``heads`` restricts the work
+    to some query heads (the others contribute nothing).
     """
     q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
     dout = np.asarray(dout, dtype=np.float64)
+    heads = range(Hq) if heads is None else heads
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -147,7 +149,7 @@ def split_attention_backward(q, k, v, dout, info, scale=None):
         for b in _members_rep_first(info, g):
             idx = sample_rows(info, b)
             L = len(idx)
-            for h in range(Hq):
+            for h in heads:
                 j = _kv_head(h, Hq, Hkv)
                 Qs, Ks, Vs = q[idx, h], k[idx, j], v[idx, j]
                 dOs = dout[idx, h].copy()

@@ -1,0 +1,320 @@
+"""Python binding of libspd: argument marshalling over the C ABI, nothing else.
+
+Every step of the path runs in the HIP library; this module only allocates
+device buffers with PyTorch, passes pointers and the current HIP stream, and
+reads back the two sizes the pages' API returns on the host (the number of
+groups and the packed length).
+
+Names follow the C ABI (``group``, ``pack``, ``pack_rows``, ``split_attn_fwd``,
+``split_attn_bwd``, ``reconstruct``) and, as aliases, the pages' calls
+("How Prompt Deduplication Works" -- Core Algorithm: ZoRRoTrain Class):
+``find_prompt_groups``, ``create_deduplicated_batch``, ``reconstruct_sequences``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from ._lib import SPD_BF16, SPD_F32, SpdAttnDesc, SpdPlan, check, lib
+
+_PLAN_FIELDS = ("group_of", "grp_off", "grp_idx", "rep", "prompt_off", "prompt_len", "resp_off", "resp_len",
+                "src", "dst", "seg_start", "counts")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Plan:
+    """Device arrays of a deduplication plan (``spd_plan``), owned here.
+
+    Capacities depend only on ``B`` and ``S``.  ``G`` and ``T`` are host copies
+    read back after grouping / packing.
+    """
+
+    def __init__(self, B: int, S: int, P: int, device):
+        self.B, self.S, self.P = int(B), int(S), int(P)
+        self.device = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=self.device)
+        n = self.B * self.S
+        self.group_of = torch.empty(self.B, **i32)
+        self.grp_off = torch.empty(self.B + 1, **i32)
+        self.grp_idx = torch.empty(self.B, **i32)
+        self.rep = torch.empty(self.B, **i32)
+        self.prompt_off = torch.empty(self.B, **i32)
+        self.prompt_len = torch.empty(self.B, **i32)
+        self.resp_off = torch.empty(self.B, **i32)
+        self.resp_len = torch.empty(self.B, **i32)
+        self.src = torch.empty(n, **i32)
+        self.dst = torch.empty(n, **i32)
+        self.seg_start = torch.empty(n, **i32)
+        self.counts = torch.zeros(4, **i32)
+        self.G: Optional[int] = None
+        self.T: Optional[int] = None
+        self.use_unpad = False
+        self._c = SpdPlan(self.B, self.S, self.P, *[t.data_ptr() for t in
+                                                    (getattr(self, f) for f in _PLAN_FIELDS)])
+
+    @property
+    def c(self) -> SpdPlan:
+        return self._c
+
+    def read_counts(self):
+        c = self.counts.cpu().tolist()
+        self.G, self.T = int(c[0]), int(c[1])
+        return self.G, self.T
+
+
+class PromptGroups(list):
+    """``prompt_groups`` as the pages return it (a list of lists of sample
+    indices), carrying the device plan it was read from."""
+
+    def __init__(self, groups, plan: Plan):
+        super().__init__(groups)
+        self.plan = plan
+
+
+class ReconstructionInfo(dict):
+    """Reconstruction metadata: the plan's device arrays by name, plus sizes."""
+
+    def __init__(self, plan: Plan):
+        super().__init__({f: getattr(plan, f) for f in _PLAN_FIELDS})
+        self.update(B=plan.B, S=plan.S, P=plan.P, G=plan.G, T=plan.T, use_unpad=plan.use_unpad)
+        self.plan = plan
+
+
+# ---------------------------------------------------------------------------- group / pack
+
+
+def group(input_ids: torch.Tensor, response_length: int, return_lists: bool = True):
+    """spd_group: samples with identical prompt ids (``input_ids [B, S]`` int64).
+
+    Returns ``(prompt_groups, unique_prompts [G, P])``.  With
+    ``return_lists=False`` the groups are not read back as Python lists
+    (``prompt_groups`` is then an empty ``PromptGroups`` with the plan).
+    """
+    _need_cuda(input_ids, "input_ids")
+    if input_ids.dtype != torch.int64 or input_ids.dim() != 2:
+        raise ValueError("input_ids must be int64 [batch, seq_len]")
+    B, S = input_ids.shape
+    P = S - int(response_length)
+    plan = Plan(B, S, P, input_ids.device)
+    ws = torch.empty(lib.spd_group_workspace_bytes(B, S), dtype=torch.uint8, device=input_ids.device)
+    uniq = torch.empty((B, P), dtype=torch.int64, device=input_ids.device)
+    check("spd_group", lib.spd_group(_ptr(input_ids), B, S, int(response_length), ctypes.byref(plan.c),
+                                     _ptr(uniq) if P > 0 else None, _ptr(ws), ws.numel(), _stream(input_ids.device)))
+    plan.G = int(plan.counts[0].item())
+    groups = []
+    if return_lists:
+        off = plan.grp_off[:plan.G + 1].cpu().tolist()
+        idx = plan.grp_idx.cpu().tolist()
+        groups = [idx[off[g]:off[g + 1]] for g in range(plan.G)]
+    return PromptGroups(groups, plan), uniq[:plan.G]
+
+
+def pack(input_ids: torch.Tensor, position_ids: torch.Tensor, response_length: int, prompt_groups: PromptGroups,
+         unique_prompts: Optional[torch.Tensor] = None, attention_mask: Optional[torch.Tensor] = None,
+         use_unpad: bool = False):
+    """spd_pack: the deduplicated ``[1, T]`` ids and positions plus reconstruction info."""
+    if not isinstance(prompt_groups, PromptGroups):
+        raise TypeError("prompt_groups must come from group()/find_prompt_groups() (it carries the device plan)")
+    plan = prompt_groups.plan
+    _need_cuda(input_ids, "input_ids")
+    _need_cuda(position_ids, "position_ids")
+    if tuple(input_ids.shape) != (plan.B, plan.S) or tuple(position_ids.shape) != (plan.B, plan.S):
+        raise ValueError("input_ids / position_ids shape does not match the grouping")
+    if plan.S - int(response_length) != plan.P:
+        raise ValueError("response_length differs from the one used for grouping")
+    if position_ids.dtype != torch.int64:
+        raise ValueError("position_ids must be int64")
+    mask_ptr, esz = None, 1
+    if attention_mask is not None:
+        _need_cuda(attention_mask, "attention_mask")
+        if tuple(attention_mask.shape) != (plan.B, plan.S):
+            raise ValueError("attention_mask shape must be [batch, seq_len]")
+        esz = attention_mask.element_size()
+        if attention_mask.dtype not in (torch.bool, torch.int8, torch.uint8, torch.int32, torch.int64):
+            raise ValueError("attention_mask must be bool or an integer type")
+        mask_ptr = _ptr(attention_mask)
+    if use_unpad and attention_mask is None:
+        raise ValueError("use_unpad=True needs attention_mask")
+    dev = input_ids.device
+    n = plan.B * plan.S
+    dids = torch.empty(n, dtype=torch.int64, device=dev)
+    dpos = torch.empty(n, dtype=torch.int64, device=dev)
+    ws = torch.empty(lib.spd_pack_workspace_bytes(plan.B, plan.S), dtype=torch.uint8, device=dev)
+    check("spd_pack", lib.spd_pack(_ptr(input_ids), _ptr(position_ids), mask_ptr, esz, int(bool(use_unpad)),
+                                   ctypes.byref(plan.c), _ptr(dids), _ptr(dpos), _ptr(ws), ws.numel(), _stream(dev)))
+    plan.use_unpad = bool(use_unpad)
+    plan.read_counts()
+    T = plan.T
+    return dids[:T].view(1, T), dpos[:T].view(1, T), ReconstructionInfo(plan)
+
+
+def pack_rows(rows: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
+    """spd_pack_rows: ``rows [B, S, ...] -> [T, ...]`` with the plan's packing."""
+    plan = info.plan
+    _need_cuda(rows, "rows")
+    if tuple(rows.shape[:2]) != (plan.B, plan.S):
+        raise ValueError("rows must be [batch, seq_len, ...]")
+    tail = tuple(rows.shape[2:])
+    row_bytes = rows[0, 0].numel() * rows.element_size()
+    out = torch.empty((plan.T,) + tail, dtype=rows.dtype, device=rows.device)
+    check("spd_pack_rows", lib.spd_pack_rows(ctypes.byref(plan.c), plan.T, _ptr(rows), row_bytes, _ptr(out),
+                                             _stream(rows.device)))
+    return out
+
+
+def reconstruct(dedup_hidden: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
+    """spd_reconstruct: ``[1, T, ...]`` or ``[T, ...]`` -> ``[B, S, ...]``."""
+    plan = info.plan
+    x = dedup_hidden
+    if x.dim() >= 3 and x.shape[0] == 1 and x.shape[1] == plan.T:
+        x = x[0]
+    _need_cuda(x, "dedup_hidden")
+    if x.shape[0] != plan.T:
+        raise ValueError(f"dedup_hidden has {x.shape[0]} rows, the plan has T = {plan.T}")
+    tail = tuple(x.shape[1:])
+    row_bytes = (x[0].numel() if x.dim() > 1 else 1) * x.element_size()
+    out = torch.empty((plan.B, plan.S) + tail, dtype=x.dtype, device=x.device)
+    check("spd_reconstruct", lib.spd_reconstruct(ctypes.byref(plan.c), plan.T, _ptr(x), row_bytes, _ptr(out),
+                                                 _stream(x.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------- attention
+
+
+def _desc(q: torch.Tensor, k: torch.Tensor, softmax_scale: Optional[float]) -> SpdAttnDesc:
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [T, Hq, d] and k, v [T, Hkv, d]")
+    T, Hq, d = q.shape
+    if k.shape[0] != T or k.shape[2] != d:
+        raise ValueError("q and k disagree on T or head_dim")
+    if q.dtype == torch.bfloat16:
+        dt = SPD_BF16
+    elif q.dtype == torch.float32:
+        dt = SPD_F32
+    else:
+        raise ValueError("attention tensors must be bfloat16 or float32")
+    scale = (1.0 / math.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    return SpdAttnDesc(Hq, k.shape[1], d, dt, scale)
+
+
+def _attn_ws(desc: SpdAttnDesc, plan: Plan, T: int, device):
+    n = lib.spd_attn_workspace_bytes(ctypes.byref(desc), plan.B, T)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def split_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, info: ReconstructionInfo,
+                   softmax_scale: Optional[float] = None):
+    """spd_split_attn_fwd: packed ``q [T,Hq,d]``, ``k, v [T,Hkv,d]`` -> ``(o, lse [Hq,T])``."""
+    plan = info.plan
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(t, name)
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v must share a dtype")
+    desc = _desc(q, k, softmax_scale)
+    T = q.shape[0]
+    if T != plan.T:
+        raise ValueError(f"q has {T} rows, the plan has T = {plan.T}")
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], T), dtype=torch.float32, device=q.device)
+    ws = _attn_ws(desc, plan, T, q.device)
+    check("spd_split_attn_fwd", lib.spd_split_attn_fwd(ctypes.byref(desc), ctypes.byref(plan.c), T, _ptr(q), _ptr(k),
+                                                       _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                                       _stream(q.device)))
+    return o, lse
+
+
+def split_attn_bwd(q, k, v, o, lse, dout, info: ReconstructionInfo, softmax_scale: Optional[float] = None):
+    """spd_split_attn_bwd: ``(dq, dk, dv)`` from the forward's ``o``, ``lse`` and ``dout``."""
+    plan = info.plan
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        _need_cuda(t, name)
+    if not (k.dtype == v.dtype == o.dtype == dout.dtype == q.dtype) or lse.dtype != torch.float32:
+        raise ValueError("q, k, v, o, dout share a dtype; lse is float32")
+    desc = _desc(q, k, softmax_scale)
+    T = q.shape[0]
+    if T != plan.T:
+        raise ValueError(f"q has {T} rows, the plan has T = {plan.T}")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = _attn_ws(desc, plan, T, q.device)
+    check("spd_split_attn_bwd", lib.spd_split_attn_bwd(ctypes.byref(desc), ctypes.byref(plan.c), T, _ptr(q), _ptr(k),
+                                                       _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                                       _ptr(dv), _ptr(ws), ws.numel(), _stream(q.device)))
+    return dq, dk, dv
+
+
+class SplitAttention(torch.autograd.Function):
+    """Autograd wrapper: forward/backward are the library's two calls."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, info, softmax_scale=None):
+        o, lse = split_attn_fwd(q, k, v, info, softmax_scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.info, ctx.scale = info, softmax_scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = split_attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.info, ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def split_attention(q, k, v, info, softmax_scale=None):
+    return SplitAttention.apply(q, k, v, info, softmax_scale)
+
+
+# ---------------------------------------------------------------------------- the pages' names
+
+
+def find_prompt_groups(input_ids: torch.Tensor, response_length: int):
+    """Finding Prompt Groups: ``(prompt_groups, unique_prompts [G, P])``."""
+    return group(input_ids, response_length)
+
+
+def create_deduplicated_batch(input_ids, position_ids, response_length, prompt_groups, unique_prompts,
+                              attention_mask=None, use_unpad=False):
+    """Creating Deduplicated Batch: ``(dedup_input_ids [1,T], dedup_position_ids [1,T], reconstruction_info)``."""
+    return pack(input_ids, position_ids, response_length, prompt_groups, unique_prompts, attention_mask, use_unpad)
+
+
+def reconstruct_sequences(dedup_hidden: torch.Tensor, reconstruction_info: ReconstructionInfo) -> torch.Tensor:
+    """Reconstructing Original Batch: ``[1, T, H] -> [B, S, H]``."""
+    return reconstruct(dedup_hidden, reconstruction_info)
+
+
+# ---------------------------------------------------------------------------- kernel timing
+
+
+def profile_begin() -> None:
+    """Start recording HIP events around the library's main kernels (this thread)."""
+    check("spd_profile_begin", lib.spd_profile_begin())
+
+
+def profile_end() -> dict:
+    """Stop recording; ``{kernel: (launches, total_ms)}`` measured on the launch streams."""
+    from ._lib import SPD_K_NAMES
+    n = len(SPD_K_NAMES)
+    launches = (ctypes.c_int64 * n)()
+    total = (ctypes.c_double * n)()
+    check("spd_profile_end", lib.spd_profile_end(launches, total))
+    return {SPD_K_NAMES[i]: (int(launches[i]), float(total[i])) for i in range(n)}

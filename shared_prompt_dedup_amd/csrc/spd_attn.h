@@ -1,0 +1,67 @@
+// Internal declarations shared by the split-attention translation units.
+//
+// Work decomposition (How Prompt Deduplication Works, Phase 2 "Split
+// Attention Optimization"): in the packed batch, group g owns the rows
+// [po, po + pl) of its prompt followed by the rows of all its members'
+// responses [ro, re), ro = po + pl.  A query row q sees
+//   * keys k <= q of its own segment (k >= seg_start[q]), and
+//   * when q is a response row, every key of its group's prompt.
+// Query tiles never straddle a prompt/response boundary or a group; response
+// query tiles may span several responses of one group (masking by seg_start
+// keeps siblings apart).  Key tiles are cut the same way.
+#pragma once
+
+#include "spd_internal.h"
+
+namespace spd {
+
+// A query tile: rows [r0, r1); unmasked prompt keys [u0, u1) (empty for
+// prompt tiles); own-segment keys start at s0 (masked by the rule above).
+// A key tile: keys [r0, r1); masked query rows [u0, u1) (the rule above);
+// unmasked query rows [s0, e0) (a prompt key tile's group responses).
+struct alignas(32) Tile {
+  int r0, r1;
+  int u0, u1;
+  int s0, e0;
+  int cost;
+  int kind;   // 0 = prompt rows, 1 = response rows
+};
+
+enum TileMode { kQueryTiles = 0, kKeyTiles = 1 };
+
+// Upper bound on the tiles of one list.
+inline int64_t tile_capacity(int64_t B, int64_t T, int rows_per_tile) {
+  return (T + rows_per_tile - 1) / rows_per_tile + 2 * B + 1;
+}
+
+// Builds a tile list on the device (one block), sorted by decreasing cost so
+// that the heaviest tiles are dispatched first.  `tmp` and `out` hold
+// `cap` tiles; *n_out receives the count.
+spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, Tile *tmp,
+                              Tile *out, int *n_out, int64_t cap, hipStream_t st);
+
+// fp32 correctness kernels (plain arithmetic, one row per thread).
+spd_status attn_fwd_f32(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *tiles,
+                        const int *ntiles, int64_t cap, const float *q, const float *k, const float *v, float *o,
+                        float *lse, hipStream_t st);
+spd_status attn_bwd_f32(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *qtiles,
+                        const int *nq, int64_t capq, const Tile *ktiles, const int *nk, int64_t capk,
+                        const float *q, const float *k, const float *v, const float *o, const float *lse,
+                        const float *dout, float *dq, float *dk, float *dv, float *Dbuf, hipStream_t st);
+
+// bf16 matrix-core kernels.
+int fwd_bf16_rows_per_tile(const spd_attn_desc &d);
+int dq_bf16_rows_per_tile(const spd_attn_desc &d);
+int dkdv_bf16_rows_per_tile(const spd_attn_desc &d);
+spd_status attn_fwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *tiles,
+                         const int *ntiles, int64_t cap, const void *q, const void *k, const void *v, void *o,
+                         float *lse, hipStream_t st);
+spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *qtiles,
+                         const int *nq, int64_t capq, const Tile *ktiles, const int *nk, int64_t capk,
+                         const void *q, const void *k, const void *v, const void *o, const float *lse,
+                         const void *dout, void *dq, void *dk, void *dv, float *Dbuf, hipStream_t st);
+
+// Rows per tile of the fp32 kernels.
+constexpr int kF32Rows = 64;
+
+}  // namespace spd

@@ -1,0 +1,227 @@
+// Split attention: tile planning on the device and the C-ABI entry points.
+//
+// How Prompt Deduplication Works -- Phase 2, "Split Attention Optimization"
+// (prompt-to-prompt once per unique prompt; response-to-full over its prompt
+// and itself) and "Correctness & Gradients".
+#include <algorithm>
+
+#include "spd_attn.h"
+
+namespace spd {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kBuckets = 4096;
+
+// Row one past the end of the response segment containing packed row x.
+__device__ inline int segment_end(const spd_plan &plan, int x) {
+  const int b = static_cast<int>(plan.src[x] / plan.S);
+  return plan.resp_off[b] + plan.resp_len[b];
+}
+
+__global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int T, int TM, int mode,
+                                                               int cap, Tile *__restrict__ tmp,
+                                                               Tile *__restrict__ out, int *__restrict__ n_out) {
+  __shared__ int scan_tmp[kPlanThreads / 64];
+  __shared__ int hist[kBuckets];
+  __shared__ int s_total;
+  const int tid = threadIdx.x;
+  const int G = plan.counts[0];
+  const int Tdev = min(plan.counts[1], T);
+  // 1. tiles per group, exclusive scan over groups, emit (one thread per group)
+  int base = 0;
+  for (int g0 = 0; g0 < G; g0 += kPlanThreads) {
+    const int g = g0 + tid;
+    int po = 0, ro = 0, re = 0, np = 0, nr = 0;
+    if (g < G) {
+      po = min(plan.prompt_off[g], Tdev);
+      ro = min(po + plan.prompt_len[g], Tdev);
+      re = (g + 1 < G) ? min(plan.prompt_off[g + 1], Tdev) : Tdev;
+      re = max(re, ro);
+      np = (ro - po + TM - 1) / TM;
+      nr = (re - ro + TM - 1) / TM;
+    }
+    int total = 0;
+    const int ex = block_exclusive_scan(np + nr, scan_tmp, total);
+    if (g < G) {
+      int idx = base + ex;
+      for (int i = 0; i < np + nr && idx < cap; ++i, ++idx) {
+        Tile t;
+        const bool prompt = i < np;
+        const int lo = prompt ? po : ro;
+        const int hi = prompt ? ro : re;
+        const int j = prompt ? i : i - np;
+        t.r0 = lo + j * TM;
+        t.r1 = min(hi, t.r0 + TM);
+        t.kind = prompt ? 0 : 1;
+        if (mode == kQueryTiles) {
+          t.u0 = prompt ? 0 : po;
+          t.u1 = prompt ? 0 : ro;
+          t.s0 = plan.seg_start[t.r0];
+          t.e0 = 0;
+          t.cost = (t.u1 - t.u0) + (t.r1 - t.s0);
+        } else {
+          t.u0 = t.r0;
+          t.u1 = prompt ? ro : segment_end(plan, t.r1 - 1);
+          t.s0 = prompt ? ro : 0;
+          t.e0 = prompt ? re : 0;
+          t.cost = (t.u1 - t.u0) + (t.e0 - t.s0);
+        }
+        tmp[idx] = t;
+      }
+    }
+    base += total;
+  }
+  const int N = min(base, cap);
+  // 2. counting sort by decreasing cost (order inside a bucket is free: it
+  //    only changes which block runs a tile first, never a result)
+  int shift = 0;
+  while ((Tdev >> shift) >= kBuckets) ++shift;
+  for (int i = tid; i < kBuckets; i += kPlanThreads) hist[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < N; i += kPlanThreads) {
+    const int bkt = kBuckets - 1 - min(tmp[i].cost >> shift, kBuckets - 1);
+    atomicAdd(&hist[bkt], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the 4096 buckets, 4 per thread
+  int c[4], s = 0;
+  for (int e = 0; e < 4; ++e) {
+    c[e] = hist[tid * 4 + e];
+    s += c[e];
+  }
+  int total = 0;
+  int ex = block_exclusive_scan(s, scan_tmp, total);
+  __syncthreads();
+  for (int e = 0; e < 4; ++e) {
+    hist[tid * 4 + e] = ex;
+    ex += c[e];
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += kPlanThreads) {
+    const Tile t = tmp[i];
+    const int bkt = kBuckets - 1 - min(t.cost >> shift, kBuckets - 1);
+    out[atomicAdd(&hist[bkt], 1)] = t;
+  }
+  if (tid == 0) *n_out = N;
+}
+
+}  // namespace
+
+spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, Tile *tmp,
+                              Tile *out, int *n_out, int64_t cap, hipStream_t st) {
+  static_assert(kBuckets == 4 * kPlanThreads, "bucket scan assumes 4 buckets per thread");
+  hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(kPlanThreads), 0, st, plan, int(T), rows_per_tile, int(mode),
+                     int(cap), tmp, out, n_out);
+  return check_launch();
+}
+
+namespace {
+
+struct AttnWs {
+  Tile *qtiles = nullptr, *ktiles = nullptr, *tmp = nullptr;
+  int *counts = nullptr;
+  float *Dbuf = nullptr;
+  int64_t capq = 0, capk = 0;
+  size_t bytes = 0;
+};
+
+int q_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : fwd_bf16_rows_per_tile(d); }
+int dq_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dq_bf16_rows_per_tile(d); }
+int k_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dkdv_bf16_rows_per_tile(d); }
+
+// Workspace: [D: Hq*T floats][query tiles][key tiles][scratch tiles][counts]
+AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
+  AttnWs w;
+  const int rq = std::min(q_rows(d), dq_rows(d));
+  w.capq = tile_capacity(B, T, rq);
+  w.capk = tile_capacity(B, T, k_rows(d));
+  const size_t dbytes = round_up(size_t(d.num_q_heads) * size_t(T) * 4, 256);
+  const size_t qb = round_up(size_t(w.capq) * sizeof(Tile), 256);
+  const size_t kb = round_up(size_t(w.capk) * sizeof(Tile), 256);
+  const size_t tb = std::max(qb, kb);
+  char *p = static_cast<char *>(base);
+  size_t off = 0;
+  if (p) w.Dbuf = reinterpret_cast<float *>(p + off);
+  off += dbytes;
+  if (p) w.qtiles = reinterpret_cast<Tile *>(p + off);
+  off += qb;
+  if (p) w.ktiles = reinterpret_cast<Tile *>(p + off);
+  off += kb;
+  if (p) w.tmp = reinterpret_cast<Tile *>(p + off);
+  off += tb;
+  if (p) w.counts = reinterpret_cast<int *>(p + off);
+  off += 256;
+  w.bytes = off;
+  return w;
+}
+
+spd_status validate_desc(const spd_attn_desc *d) {
+  if (!d) return SPD_ERR_INVALID_ARG;
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads) return SPD_ERR_INVALID_ARG;
+  if (!(d->softmax_scale > 0.0f)) return SPD_ERR_INVALID_ARG;
+  if (d->dtype != SPD_F32 && d->dtype != SPD_BF16) return SPD_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return SPD_ERR_UNSUPPORTED;
+  if (d->num_q_heads > 1024) return SPD_ERR_UNSUPPORTED;
+  return SPD_OK;
+}
+
+spd_status validate_common(const spd_attn_desc *d, const spd_plan *plan, int64_t T, void *ws, size_t ws_bytes) {
+  SPD_TRY(validate_desc(d));
+  SPD_TRY(validate_plan(plan));
+  if (T < 0 || T > plan->B * plan->S) return SPD_ERR_INVALID_ARG;
+  if (int64_t(d->num_q_heads) * T * d->head_dim >= (int64_t(1) << 40)) return SPD_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < spd_attn_workspace_bytes(d, plan->B, T)) return SPD_ERR_WORKSPACE;
+  return SPD_OK;
+}
+
+}  // namespace
+}  // namespace spd
+
+using namespace spd;
+
+extern "C" size_t spd_attn_workspace_bytes(const spd_attn_desc *desc, int64_t B, int64_t T) {
+  if (validate_desc(desc) != SPD_OK || B < 1 || T < 0) return 0;
+  return carve(*desc, B, T, nullptr).bytes;
+}
+
+extern "C" spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T, const void *q,
+                                         const void *k, const void *v, void *o, float *lse, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+  SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes));
+  if (!q || !k || !v || !o || !lse) return SPD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return SPD_ERR_ALIGNMENT;
+  if (T == 0) return SPD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AttnWs w = carve(*desc, plan->B, T, workspace);
+  SPD_TRY(launch_build_tiles(*plan, T, q_rows(*desc), kQueryTiles, w.tmp, w.qtiles, w.counts, w.capq, st));
+  if (desc->dtype == SPD_F32)
+    return attn_fwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, static_cast<const float *>(q),
+                        static_cast<const float *>(k), static_cast<const float *>(v), static_cast<float *>(o), lse,
+                        st);
+  return attn_fwd_bf16(*desc, *plan, T, w.qtiles, w.counts, w.capq, q, k, v, o, lse, st);
+}
+
+extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T, const void *q,
+                                         const void *k, const void *v, const void *o, const float *lse,
+                                         const void *dout, void *dq, void *dk, void *dv, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+  SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes));
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPD_ERR_INVALID_ARG;
+  for (const void *p : {q, k, v, o, static_cast<const void *>(lse), dout, static_cast<const void *>(dq),
+                        static_cast<const void *>(dk), static_cast<const void *>(dv)})
+    if (!aligned16(p)) return SPD_ERR_ALIGNMENT;
+  if (T == 0) return SPD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AttnWs w = carve(*desc, plan->B, T, workspace);
+  SPD_TRY(launch_build_tiles(*plan, T, dq_rows(*desc), kQueryTiles, w.tmp, w.qtiles, w.counts, w.capq, st));
+  SPD_TRY(launch_build_tiles(*plan, T, k_rows(*desc), kKeyTiles, w.tmp, w.ktiles, w.counts + 1, w.capk, st));
+  if (desc->dtype == SPD_F32)
+    return attn_bwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, w.ktiles, w.counts + 1, w.capk,
+                        static_cast<const float *>(q), static_cast<const float *>(k), static_cast<const float *>(v),
+                        static_cast<const float *>(o), lse, static_cast<const float *>(dout),
+                        static_cast<float *>(dq), static_cast<float *>(dk), static_cast<float *>(dv), w.Dbuf, st);
+  return attn_bwd_bf16(*desc, *plan, T, w.qtiles, w.counts, w.capq, w.ktiles, w.counts + 1, w.capk, q, k, v, o, lse,
+                       dout, dq, dk, dv, w.Dbuf, st);
+}

@@ -1,0 +1,578 @@
+// Grouping, packing, row packing and reconstruction kernels plus their C-ABI
+// entry points.  All of this is exact integer / byte work.
+//
+// How Prompt Deduplication Works:
+//   Core Algorithm -- "Finding Prompt Groups", "Creating Deduplicated Batch",
+//   "Reconstructing Original Batch"; "Working with Packed/Unpacked Sequences";
+//   Phase 1 (prompt detection & deduplication) and Phase 3 (reconstruction).
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "spd_internal.h"
+
+namespace spd {
+
+namespace {
+thread_local int g_last_hip_error = 0;
+}
+
+void set_last_hip_error(hipError_t e) { g_last_hip_error = static_cast<int>(e); }
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= static_cast<int>(cache.size())) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+spd_status validate_plan(const spd_plan *p) {
+  if (!p) return SPD_ERR_INVALID_ARG;
+  if (p->B < 1 || p->B > 65536 || p->S < 1 || p->P < 0 || p->P > p->S) return SPD_ERR_INVALID_ARG;
+  if (p->B * p->S >= (int64_t(1) << 31)) return SPD_ERR_UNSUPPORTED;
+  if (!p->group_of || !p->grp_off || !p->grp_idx || !p->rep || !p->prompt_off || !p->prompt_len ||
+      !p->resp_off || !p->resp_len || !p->src || !p->dst || !p->seg_start || !p->counts)
+    return SPD_ERR_INVALID_ARG;
+  return SPD_OK;
+}
+
+// ----------------------------------------------------------------------------
+// Grouping
+// ----------------------------------------------------------------------------
+
+// splitmix64 finalizer (Steele, Lea & Flood, "Fast splittable pseudorandom
+// number generators", 2014): a bijective 64-bit mixer.
+__device__ inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// One block per row: an order-dependent hash of the row's P prompt ids, the
+// wrapping sum of mix64(id + position * golden-ratio constant).  It only
+// narrows the candidates; equality is always decided by full comparison.
+__global__ void __launch_bounds__(256) k_hash_rows(const int64_t *__restrict__ ids, int64_t S, int64_t P,
+                                                    uint64_t *__restrict__ hash) {
+  const int64_t b = blockIdx.x;
+  const int64_t *row = ids + b * S;
+  uint64_t h = 0;
+  for (int64_t t = threadIdx.x; t < P; t += blockDim.x)
+    h += mix64(static_cast<uint64_t>(row[t]) + static_cast<uint64_t>(t + 1) * 0x9E3779B97F4A7C15ull);
+  __shared__ uint64_t part[4];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) h += __shfl_xor(h, off, 64);
+  if (__lane_id() == 0) part[threadIdx.x / 64] = h;
+  __syncthreads();
+  if (threadIdx.x == 0) hash[b] = part[0] + part[1] + part[2] + part[3];
+}
+
+// One block per row b: rep_of[b] = the smallest c <= b whose prompt equals
+// row b's.  Candidates are scanned in ascending order in chunks of 256; only
+// equal hashes are compared in full.
+__global__ void __launch_bounds__(256) k_find_rep(const int64_t *__restrict__ ids, int64_t S, int64_t P,
+                                                   const uint64_t *__restrict__ hash,
+                                                   int32_t *__restrict__ rep_of) {
+  const int b = blockIdx.x;
+  const uint64_t hb = hash[b];
+  const int64_t *rowb = ids + int64_t(b) * S;
+  __shared__ int cand[256];
+  for (int c0 = 0; c0 < b; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    cand[threadIdx.x] = (c < b && hash[c] == hb) ? 1 : 0;
+    __syncthreads();
+    const int n = min(256, b - c0);
+    for (int i = 0; i < n; ++i) {
+      if (!cand[i]) continue;   // uniform: every thread reads the same flag
+      const int64_t *rowc = ids + int64_t(c0 + i) * S;
+      int diff = 0;
+      for (int64_t t = threadIdx.x; t < P; t += blockDim.x) diff |= (rowc[t] != rowb[t]);
+      if (!__syncthreads_or(diff)) {
+        if (threadIdx.x == 0) rep_of[b] = c0 + i;
+        return;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) rep_of[b] = b;
+}
+
+// Single block: number groups by first occurrence, build group_of, CSR
+// offsets and the member lists (ascending), and counts[0] = G.
+constexpr int kFinalThreads = 1024;
+__global__ void __launch_bounds__(kFinalThreads) k_finalize_groups(int B, const int32_t *__restrict__ rep_of,
+                                                                    int32_t *__restrict__ gid_of,
+                                                                    int32_t *__restrict__ fill,
+                                                                    spd_plan plan) {
+  __shared__ int scan_tmp[kFinalThreads / 64];
+  __shared__ int chunk_g[kFinalThreads];
+  const int tid = threadIdx.x;
+  // A: group ids for first members, in ascending order of the first member.
+  int running = 0;
+  for (int b0 = 0; b0 < B; b0 += kFinalThreads) {
+    const int b = b0 + tid;
+    const int is_rep = (b < B && rep_of[b] == b) ? 1 : 0;
+    int total = 0;
+    const int ex = block_exclusive_scan(is_rep, scan_tmp, total);
+    if (is_rep) {
+      gid_of[b] = running + ex;
+      plan.rep[running + ex] = b;
+    }
+    running += total;
+  }
+  const int G = running;
+  for (int g = tid; g < B; g += kFinalThreads) fill[g] = 0;
+  __syncthreads();
+  // B: group of every sample and member counts.
+  for (int b = tid; b < B; b += kFinalThreads) {
+    const int g = gid_of[rep_of[b]];
+    plan.group_of[b] = g;
+    atomicAdd(&fill[g], 1);
+  }
+  __syncthreads();
+  // C: CSR offsets.
+  int base = 0;
+  for (int g0 = 0; g0 < G; g0 += kFinalThreads) {
+    const int g = g0 + tid;
+    const int c = g < G ? fill[g] : 0;
+    int total = 0;
+    const int ex = block_exclusive_scan(c, scan_tmp, total);
+    if (g < G) plan.grp_off[g] = base + ex;
+    base += total;
+  }
+  if (tid == 0) {
+    plan.grp_off[G] = B;
+    plan.counts[0] = G;
+  }
+  __syncthreads();
+  for (int g = tid; g < G; g += kFinalThreads) fill[g] = 0;
+  __syncthreads();
+  // D: stable placement of members (ascending sample index within a group).
+  for (int b0 = 0; b0 < B; b0 += kFinalThreads) {
+    const int b = b0 + tid;
+    const int n = min(kFinalThreads, B - b0);
+    const int g = b < B ? plan.group_of[b] : -1;
+    chunk_g[tid] = g;
+    __syncthreads();
+    int rank = 0, later = 0, slot = -1;
+    if (b < B) {
+      for (int i = 0; i < n; ++i) {
+        if (chunk_g[i] == g) {
+          rank += (i < tid);
+          later += (i > tid);
+        }
+      }
+      slot = plan.grp_off[g] + fill[g] + rank;
+    }
+    __syncthreads();   // every thread has read fill[] for this chunk
+    if (b < B) {
+      plan.grp_idx[slot] = b;
+      if (later == 0) fill[g] += rank + 1;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(256) k_unique_prompts(const int64_t *__restrict__ ids, int64_t S, int64_t P,
+                                                         const int32_t *__restrict__ rep,
+                                                         const int32_t *__restrict__ counts,
+                                                         int64_t *__restrict__ out) {
+  const int g = blockIdx.x;
+  if (g >= counts[0]) return;
+  const int64_t *row = ids + int64_t(rep[g]) * S;
+  for (int64_t t = threadIdx.x; t < P; t += blockDim.x) out[int64_t(g) * P + t] = row[t];
+}
+
+// ----------------------------------------------------------------------------
+// Packing
+// ----------------------------------------------------------------------------
+
+__device__ inline bool mask_at(const void *mask, int esz, int64_t i) {
+  if (esz == 1) return static_cast<const int8_t *>(mask)[i] != 0;
+  if (esz == 4) return static_cast<const int32_t *>(mask)[i] != 0;
+  return static_cast<const int64_t *>(mask)[i] != 0;
+}
+
+// Counts the kept tokens of [t0, t1) of one row (block-wide).
+__device__ inline int block_count_kept(const void *mask, int esz, int64_t row_base, int64_t t0, int64_t t1) {
+  int c = 0;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) c += mask_at(mask, esz, row_base + t);
+  __shared__ int part[4];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+  __syncthreads();
+  if (__lane_id() == 0) part[threadIdx.x / 64] = c;
+  __syncthreads();
+  return part[0] + part[1] + part[2] + part[3];
+}
+
+// One block per sample: kept response tokens, and the kept prompt tokens of
+// its group when the sample is the group's first member.
+__global__ void __launch_bounds__(256) k_seg_lengths(int64_t S, int64_t P, const void *mask, int esz,
+                                                      int unpad, spd_plan plan) {
+  const int b = blockIdx.x;
+  const int g = plan.group_of[b];
+  const bool first = plan.rep[g] == b;
+  int r, p = 0;
+  if (unpad) {
+    r = block_count_kept(mask, esz, int64_t(b) * S, P, S);
+    if (first) p = block_count_kept(mask, esz, int64_t(b) * S, 0, P);
+  } else {
+    r = static_cast<int>(S - P);
+    p = static_cast<int>(P);
+  }
+  if (threadIdx.x == 0) {
+    plan.resp_len[b] = r;
+    if (first) plan.prompt_len[g] = p;
+  }
+}
+
+// Single block: segment order [prompt g][members of g ascending]..., exclusive
+// scan of segment lengths -> prompt_off / resp_off, counts[1] = T.
+__global__ void __launch_bounds__(kFinalThreads) k_seg_offsets(int B, int32_t *__restrict__ seg, spd_plan plan) {
+  __shared__ int scan_tmp[kFinalThreads / 64];
+  const int G = plan.counts[0];
+  const int nseg = G + B;
+  for (int g = threadIdx.x; g < G; g += kFinalThreads) seg[plan.grp_off[g] + g] = plan.prompt_len[g];
+  for (int i = threadIdx.x; i < B; i += kFinalThreads) {
+    const int b = plan.grp_idx[i];
+    seg[i + plan.group_of[b] + 1] = plan.resp_len[b];
+  }
+  __syncthreads();
+  int base = 0;
+  for (int s0 = 0; s0 < nseg; s0 += kFinalThreads) {
+    const int s = s0 + threadIdx.x;
+    const int len = s < nseg ? seg[s] : 0;
+    int total = 0;
+    const int ex = block_exclusive_scan(len, scan_tmp, total);
+    __syncthreads();
+    if (s < nseg) seg[s] = base + ex;
+    base += total;
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += kFinalThreads) plan.prompt_off[g] = seg[plan.grp_off[g] + g];
+  for (int i = threadIdx.x; i < B; i += kFinalThreads) {
+    const int b = plan.grp_idx[i];
+    plan.resp_off[b] = seg[i + plan.group_of[b] + 1];
+  }
+  if (threadIdx.x == 0) {
+    plan.counts[1] = base;
+    plan.counts[2] = 0;
+  }
+}
+
+// Walks columns [t0, t1) of a row in order, 256 at a time, giving each kept
+// column its rank among the kept columns (ballot + popcount per wave).
+template <typename F>
+__device__ inline void for_kept_columns(const void *mask, int esz, int unpad, int64_t mask_row, int64_t t0,
+                                        int64_t t1, F &&fn) {
+  __shared__ int wave_cnt[4];
+  int running = 0;
+  const int wid = threadIdx.x / 64;
+  const uint64_t lt = (uint64_t(1) << __lane_id()) - 1;
+  for (int64_t c0 = t0; c0 < t1; c0 += blockDim.x) {
+    const int64_t t = c0 + threadIdx.x;
+    const bool in = t < t1;
+    const bool kept = in && (!unpad || mask_at(mask, esz, mask_row + t));
+    const uint64_t bal = __ballot(kept);
+    __syncthreads();
+    if (__lane_id() == 0) wave_cnt[wid] = __popcll(bal);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < 4; ++w) {
+      before += (w < wid) ? wave_cnt[w] : 0;
+      total += wave_cnt[w];
+    }
+    if (in) fn(t, kept, running + before + __popcll(bal & lt));
+    running += total;
+  }
+}
+
+// One block per sample: dst for every (b, t); src, seg_start, dedup ids and
+// positions for the packed rows this sample owns (its response, and its
+// group's prompt when it is the first member).
+__global__ void __launch_bounds__(256) k_scatter(int64_t S, int64_t P, const int64_t *__restrict__ ids,
+                                                  const int64_t *__restrict__ pos, const void *mask, int esz,
+                                                  int unpad, spd_plan plan, int64_t *__restrict__ dids,
+                                                  int64_t *__restrict__ dpos) {
+  const int b = blockIdx.x;
+  const int g = plan.group_of[b];
+  const int r = plan.rep[g];
+  const int po = plan.prompt_off[g];
+  const int ro = plan.resp_off[b];
+  int pads = 0;
+  // prompt columns: kept-ness and positions come from the first member
+  for_kept_columns(mask, esz, unpad, int64_t(r) * S, 0, P, [&](int64_t t, bool kept, int rank) {
+    const int j = po + rank;
+    plan.dst[int64_t(b) * S + t] = kept ? j : -1;
+    pads += !kept;
+    if (kept && b == r) {
+      const int64_t s = int64_t(r) * S + t;
+      plan.src[j] = static_cast<int32_t>(s);
+      plan.seg_start[j] = po;
+      dids[j] = ids[s];
+      dpos[j] = pos[s];
+    }
+  });
+  for_kept_columns(mask, esz, unpad, int64_t(b) * S, P, S, [&](int64_t t, bool kept, int rank) {
+    const int j = ro + rank;
+    const int64_t s = int64_t(b) * S + t;
+    plan.dst[s] = kept ? j : -1;
+    pads += !kept;
+    if (kept) {
+      plan.src[j] = static_cast<int32_t>(s);
+      plan.seg_start[j] = ro;
+      dids[j] = ids[s];
+      dpos[j] = pos[s];
+    }
+  });
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) pads += __shfl_xor(pads, off, 64);
+  if (__lane_id() == 0 && pads) atomicAdd(&plan.counts[2], pads);
+}
+
+// ----------------------------------------------------------------------------
+// Row movement: pack_rows and reconstruct.  One wave moves one row of
+// row_bytes in 16-byte lanes; kU chunks per lane are loaded before any store
+// so that each wave keeps several loads in flight.
+// ----------------------------------------------------------------------------
+
+constexpr int kRowThreads = 256;
+constexpr int kU = 4;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Output rows are written once and not re-read by this kernel: non-temporal.
+__device__ inline void stream_store(u32x4 *p, const u32x4 &v) { __builtin_nontemporal_store(v, p); }
+
+__global__ void __launch_bounds__(kRowThreads) k_pack_rows(int64_t T, int64_t vec_per_row,
+                                                            const int32_t *__restrict__ src,
+                                                            const u32x4 *__restrict__ rows,
+                                                            u32x4 *__restrict__ packed) {
+  const int lane = __lane_id();
+  const int64_t nwaves = int64_t(gridDim.x) * (kRowThreads / 64);
+  for (int64_t j = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; j < T; j += nwaves) {
+    const u32x4 *in = rows + int64_t(src[j]) * vec_per_row;
+    u32x4 *out = packed + j * vec_per_row;
+    for (int64_t c0 = 0; c0 < vec_per_row; c0 += 64 * kU) {
+      u32x4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < vec_per_row) v[u] = in[c];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < vec_per_row) stream_store(out + c, v[u]);
+      }
+    }
+  }
+}
+
+// Packed row j goes to every (b, t) that maps to it: for a prompt row, the
+// same column t of every member of the group (read once, written n times);
+// for a response row, its own (b, t).
+__global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t S, int64_t P,
+                                                              int64_t vec_per_row, spd_plan plan,
+                                                              const u32x4 *__restrict__ packed,
+                                                              u32x4 *__restrict__ out) {
+  const int lane = __lane_id();
+  const int64_t nwaves = int64_t(gridDim.x) * (kRowThreads / 64);
+  for (int64_t j = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; j < T; j += nwaves) {
+    const int64_t s = plan.src[j];
+    const int64_t b0 = s / S;
+    const int64_t t = s - b0 * S;
+    int m0 = 0, m1 = 1;
+    const int32_t *members = nullptr;
+    if (t < P) {
+      const int g = plan.group_of[b0];
+      m0 = plan.grp_off[g];
+      m1 = plan.grp_off[g + 1];
+      members = plan.grp_idx;
+    }
+    const u32x4 *in = packed + j * vec_per_row;
+    for (int64_t c0 = 0; c0 < vec_per_row; c0 += 64 * kU) {
+      u32x4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < vec_per_row) v[u] = in[c];
+      }
+      for (int m = m0; m < m1; ++m) {
+        const int64_t b = members ? members[m] : b0;
+        u32x4 *o = out + (b * S + t) * vec_per_row;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int64_t c = c0 + u * 64 + lane;
+          if (c < vec_per_row) stream_store(o + c, v[u]);
+        }
+      }
+    }
+  }
+}
+
+// Zeros every output row that no packed token maps to (dst == -1).
+__global__ void __launch_bounds__(kRowThreads) k_zero_unmapped(int64_t rows, int64_t vec_per_row,
+                                                                const int32_t *__restrict__ dst,
+                                                                const int32_t *__restrict__ counts,
+                                                                u32x4 *__restrict__ out) {
+  if (counts[2] == 0) return;
+  const int lane = __lane_id();
+  const int64_t nwaves = int64_t(gridDim.x) * (kRowThreads / 64);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t r = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; r < rows; r += nwaves) {
+    if (dst[r] >= 0) continue;
+    u32x4 *o = out + r * vec_per_row;
+    for (int64_t c = lane; c < vec_per_row; c += 64) stream_store(o + c, z);
+  }
+}
+
+int row_grid(int64_t rows) {
+  const int64_t waves_per_block = kRowThreads / 64;
+  const int64_t want = (rows + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = int64_t(device_cu_count()) * 16;
+  return static_cast<int>(std::max<int64_t>(1, std::min(want, cap)));
+}
+
+}  // namespace spd
+
+using namespace spd;
+
+// ----------------------------------------------------------------------------
+// C ABI
+// ----------------------------------------------------------------------------
+
+extern "C" size_t spd_group_workspace_bytes(int64_t B, int64_t S) {
+  (void)S;
+  if (B < 1) return 0;
+  return round_up(size_t(B) * 8, 256) + 3 * round_up(size_t(B) * 4, 256);
+}
+
+extern "C" spd_status spd_group(const int64_t *input_ids, int64_t B, int64_t S, int64_t response_length,
+                                const spd_plan *plan, int64_t *unique_prompts, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  SPD_TRY(validate_plan(plan));
+  if (!input_ids || B != plan->B || S != plan->S || response_length < 0 || response_length > S ||
+      plan->P != S - response_length)
+    return SPD_ERR_INVALID_ARG;
+  if (!aligned16(input_ids) || (unique_prompts && !aligned16(unique_prompts))) return SPD_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < spd_group_workspace_bytes(B, S)) return SPD_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t P = plan->P;
+  char *ws = static_cast<char *>(workspace);
+  uint64_t *hash = reinterpret_cast<uint64_t *>(ws);
+  ws += round_up(size_t(B) * 8, 256);
+  int32_t *rep_of = reinterpret_cast<int32_t *>(ws);
+  ws += round_up(size_t(B) * 4, 256);
+  int32_t *gid_of = reinterpret_cast<int32_t *>(ws);
+  ws += round_up(size_t(B) * 4, 256);
+  int32_t *fill = reinterpret_cast<int32_t *>(ws);
+
+  hipLaunchKernelGGL(k_hash_rows, dim3(B), dim3(256), 0, st, input_ids, S, P, hash);
+  SPD_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_find_rep, dim3(B), dim3(256), 0, st, input_ids, S, P, hash, rep_of);
+  SPD_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_finalize_groups, dim3(1), dim3(kFinalThreads), 0, st, int(B), rep_of, gid_of, fill,
+                     *plan);
+  SPD_LAUNCH_CHECK();
+  if (unique_prompts && P > 0) {
+    hipLaunchKernelGGL(k_unique_prompts, dim3(B), dim3(256), 0, st, input_ids, S, P, plan->rep, plan->counts,
+                       unique_prompts);
+    SPD_LAUNCH_CHECK();
+  }
+  return SPD_OK;
+}
+
+extern "C" size_t spd_pack_workspace_bytes(int64_t B, int64_t S) {
+  (void)S;
+  if (B < 1) return 0;
+  return round_up(size_t(2 * B) * 4, 256);
+}
+
+extern "C" spd_status spd_pack(const int64_t *input_ids, const int64_t *position_ids, const void *attention_mask,
+                               int32_t mask_elem_bytes, int32_t use_unpad, const spd_plan *plan,
+                               int64_t *dedup_ids, int64_t *dedup_pos, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  SPD_TRY(validate_plan(plan));
+  if (!input_ids || !position_ids || !dedup_ids || !dedup_pos) return SPD_ERR_INVALID_ARG;
+  if (use_unpad != 0 && use_unpad != 1) return SPD_ERR_INVALID_ARG;
+  if (use_unpad && !attention_mask) return SPD_ERR_INVALID_ARG;
+  if (attention_mask && mask_elem_bytes != 1 && mask_elem_bytes != 4 && mask_elem_bytes != 8)
+    return SPD_ERR_INVALID_ARG;
+  if (!aligned16(input_ids) || !aligned16(position_ids) || !aligned16(dedup_ids) || !aligned16(dedup_pos))
+    return SPD_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < spd_pack_workspace_bytes(plan->B, plan->S)) return SPD_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t B = plan->B, S = plan->S, P = plan->P;
+  const int esz = attention_mask ? mask_elem_bytes : 1;
+  int32_t *seg = static_cast<int32_t *>(workspace);
+  hipLaunchKernelGGL(k_seg_lengths, dim3(B), dim3(256), 0, st, S, P, attention_mask, esz, use_unpad, *plan);
+  SPD_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_seg_offsets, dim3(1), dim3(kFinalThreads), 0, st, int(B), seg, *plan);
+  SPD_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_scatter, dim3(B), dim3(256), 0, st, S, P, input_ids, position_ids, attention_mask, esz,
+                     use_unpad, *plan, dedup_ids, dedup_pos);
+  SPD_LAUNCH_CHECK();
+  return SPD_OK;
+}
+
+extern "C" spd_status spd_pack_rows(const spd_plan *plan, int64_t T, const void *rows, int64_t row_bytes,
+                                    void *packed, void *stream) {
+  SPD_TRY(validate_plan(plan));
+  if (!rows || !packed || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if (row_bytes % 16 || !aligned16(rows) || !aligned16(packed)) return SPD_ERR_ALIGNMENT;
+  if (T == 0) return SPD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  prof_start(SPD_K_PACK_ROWS, st);
+  hipLaunchKernelGGL(k_pack_rows, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, row_bytes / 16, plan->src,
+                     static_cast<const u32x4 *>(rows), static_cast<u32x4 *>(packed));
+  SPD_LAUNCH_CHECK();
+  prof_stop(SPD_K_PACK_ROWS, st);
+  return SPD_OK;
+}
+
+extern "C" spd_status spd_reconstruct(const spd_plan *plan, int64_t T, const void *packed, int64_t row_bytes,
+                                      void *out, void *stream) {
+  SPD_TRY(validate_plan(plan));
+  if (!packed || !out || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if (row_bytes % 16 || !aligned16(packed) || !aligned16(out)) return SPD_ERR_ALIGNMENT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t vpr = row_bytes / 16;
+  prof_start(SPD_K_RECONSTRUCT, st);
+  if (T > 0) {
+    hipLaunchKernelGGL(k_reconstruct, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, plan->S, plan->P, vpr,
+                       *plan, static_cast<const u32x4 *>(packed), static_cast<u32x4 *>(out));
+    SPD_LAUNCH_CHECK();
+  }
+  const int64_t rows = plan->B * plan->S;
+  hipLaunchKernelGGL(k_zero_unmapped, dim3(row_grid(rows)), dim3(kRowThreads), 0, st, rows, vpr, plan->dst,
+                     plan->counts, static_cast<u32x4 *>(out));
+  SPD_LAUNCH_CHECK();
+  prof_stop(SPD_K_RECONSTRUCT, st);
+  return SPD_OK;
+}
+
+extern "C" const char *spd_status_string(spd_status s) {
+  switch (s) {
+    case SPD_OK: return "ok";
+    case SPD_ERR_INVALID_ARG: return "invalid argument";
+    case SPD_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SPD_ERR_ALIGNMENT: return "pointer or row size not 16-byte aligned";
+    case SPD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SPD_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+extern "C" int spd_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" int spd_version(void) { return 100; }

@@ -1,0 +1,152 @@
+"""GPU parity: grouping, packing, row packing and reconstruction are bit-exact
+with the oracle, on every workload at full size and on edge cases."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import gpu_plan, oracle_plan, say
+from workloads import WORKLOADS, Workload, make_batch
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    WORKLOADS["tiny_fp32"],
+    WORKLOADS["tiny_fp32"].scaled(name="ragged_unpad", num_prompts=3, rollout_n=5, prompt_len=300,
+                                  response_len=77, resp_len_range=(0, 77), seed=21),
+    WORKLOADS["tiny_fp32"].scaled(name="singletons", num_prompts=7, rollout_n=1, prompt_len=5,
+                                  response_len=3, seed=22),
+    WORKLOADS["tiny_fp32"].scaled(name="one_sample", num_prompts=1, rollout_n=1, prompt_len=9,
+                                  response_len=4, seed=23),
+    WORKLOADS["tiny_fp32"].scaled(name="many_rows", num_prompts=40, rollout_n=30, prompt_len=17,
+                                  response_len=5, vocab=3, seed=24),
+]
+CASES = [(w, p) for w in SMALL for p in (False, True)] + \
+        [(WORKLOADS[n], False) for n in WORKLOADS if n != "tiny_fp32"]
+
+
+def _ids(w, p):
+    return f"{w.name}{'-perm' if p else ''}"
+
+
+def _check_plan(bt, use_unpad, mask_dtype=None):
+    og, ou, odids, odpos, oinfo = oracle_plan(bt, use_unpad)
+    gg, gu, gdids, gdpos, ginfo = gpu_plan(bt, use_unpad, mask_dtype)
+    assert list(gg) == og
+    np.testing.assert_array_equal(gu.cpu().numpy(), ou)
+    assert ginfo["G"] == oinfo["G"] and ginfo["T"] == oinfo["T"]
+    np.testing.assert_array_equal(gdids.cpu().numpy(), odids)
+    np.testing.assert_array_equal(gdpos.cpu().numpy(), odpos)
+    G, B, T = oinfo["G"], oinfo["B"], oinfo["T"]
+    p = ginfo.plan
+    np.testing.assert_array_equal(p.group_of.cpu().numpy(), oinfo["group_of"])
+    np.testing.assert_array_equal(p.rep[:G].cpu().numpy(), oinfo["rep"])
+    np.testing.assert_array_equal(p.prompt_off[:G].cpu().numpy(), oinfo["prompt_off"])
+    np.testing.assert_array_equal(p.prompt_len[:G].cpu().numpy(), oinfo["prompt_len"])
+    np.testing.assert_array_equal(p.resp_off.cpu().numpy(), oinfo["resp_off"])
+    np.testing.assert_array_equal(p.resp_len.cpu().numpy(), oinfo["resp_len"])
+    np.testing.assert_array_equal(p.src[:T].cpu().numpy(), oinfo["src"])
+    np.testing.assert_array_equal(p.dst.cpu().numpy(), oinfo["dst"])
+    np.testing.assert_array_equal(p.seg_start[:T].cpu().numpy(), oinfo["seg_start"])
+    off = [0]
+    for m in og:
+        off.append(off[-1] + len(m))
+    np.testing.assert_array_equal(p.grp_off[:G + 1].cpu().numpy(), off)
+    np.testing.assert_array_equal(p.grp_idx.cpu().numpy(), sum(og, []))
+    return oinfo, ginfo
+
+
+@pytest.mark.parametrize("w,permute", CASES, ids=[_ids(*c) for c in CASES])
+def test_plan_bit_exact(w, permute):
+    say(f"[dedup plan] {w.name} permute={permute} B={w.batch} S={w.seq_len} unpad={w.use_unpad}")
+    _check_plan(make_batch(w, permute=permute), w.use_unpad)
+
+
+@pytest.mark.parametrize("mask_dtype", ["bool", "int32", "int64"])
+def test_mask_dtypes(mask_dtype):
+    w = SMALL[1]
+    say(f"[dedup plan] mask dtype {mask_dtype}")
+    _check_plan(make_batch(w, permute=True), True, getattr(torch, mask_dtype))
+
+
+def test_padded_mode_ignores_mask_and_prompt_padding():
+    """use_unpad=False keeps every token; use_unpad=True drops left-padded prompt tokens too."""
+    rng = np.random.default_rng(9)
+    B, P, R = 9, 40, 12
+    ids = rng.integers(1, 50, size=(B, P + R))
+    ids[:5, :P] = ids[0, :P]
+    ids[5:, :P] = ids[5, :P]
+    mask = np.ones_like(ids)
+    mask[:5, :7] = 0
+    mask[2, P + 3:] = 0
+    mask[6, P:] = 0
+    pos = np.cumsum(mask, 1) - 1
+    from workloads import Batch
+    bt = Batch(ids, pos, mask, R, None, None)
+    for unpad in (False, True):
+        say(f"[dedup plan] handmade padding unpad={unpad}")
+        _check_plan(bt, unpad)
+
+
+def test_response_length_extremes():
+    w = SMALL[0]
+    bt = make_batch(w)
+    from workloads import Batch
+    for R in (0, w.seq_len, 1):
+        say(f"[dedup plan] response_length={R}")
+        _check_plan(Batch(bt.input_ids, bt.position_ids, bt.attention_mask, R, None, None), False)
+
+
+ROW_CASES = [(SMALL[0], 512), (SMALL[1], 48), (SMALL[4], 16), (WORKLOADS["qwen3_0p6b_2x8_p8192_r512"], 4096),
+             (WORKLOADS["long_2x8_p32768_r256to1024_unpad"], 64), (WORKLOADS["bwd_4x8_p4096_r1024"], 160)]
+
+
+@pytest.mark.parametrize("w,row_bytes", ROW_CASES, ids=[f"{w.name}-{r}B" for w, r in ROW_CASES])
+def test_pack_rows_and_reconstruct_bit_exact(w, row_bytes):
+    import shared_prompt_dedup_amd as spd
+    say(f"[rows] {w.name} row_bytes={row_bytes}")
+    bt = make_batch(w, permute=True)
+    _, _, _, _, oinfo = oracle_plan(bt, w.use_unpad)
+    _, _, _, _, ginfo = gpu_plan(bt, w.use_unpad)
+    rng = np.random.default_rng(5)
+    B, S, T = oinfo["B"], oinfo["S"], oinfo["T"]
+    W = row_bytes // 4
+    # reconstruct: packed rows -> batch
+    packed = rng.integers(-2**31, 2**31 - 1, size=(T, W), dtype=np.int64).astype(np.int32)
+    out = spd.reconstruct_sequences(torch.from_numpy(packed).cuda()[None], ginfo)
+    ref = oracle.reconstruct_sequences(packed[None], oinfo)
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
+    del out
+    # pack_rows: batch rows -> packed (prompt rows equal within a group)
+    rows = rng.integers(-2**31, 2**31 - 1, size=(B, S, W), dtype=np.int64).astype(np.int32)
+    got = spd.pack_rows(torch.from_numpy(rows).cuda(), ginfo)
+    np.testing.assert_array_equal(got.cpu().numpy(), oracle.pack_rows(rows, oinfo))
+
+
+def test_reconstruct_bf16_hidden_shape():
+    """The pages' shape contract: [1, T, H] in, [B, S, H] out, for an H of hidden size."""
+    import shared_prompt_dedup_amd as spd
+    w = WORKLOADS["tiny_fp32"]
+    bt = make_batch(w)
+    _, _, _, _, oinfo = oracle_plan(bt, False)
+    _, _, _, _, ginfo = gpu_plan(bt, False)
+    H = 1024
+    x = torch.randn(1, oinfo["T"], H, dtype=torch.bfloat16, device="cuda")
+    y = spd.reconstruct_sequences(x, ginfo)
+    assert tuple(y.shape) == (w.batch, w.seq_len, H)
+    ref = oracle.reconstruct_sequences(x.float().cpu().numpy(), oinfo)
+    np.testing.assert_array_equal(y.float().cpu().numpy(), ref)
+
+
+def test_repeat_calls_are_identical():
+    import shared_prompt_dedup_amd as spd
+    w = SMALL[1]
+    bt = make_batch(w, permute=True)
+    a = gpu_plan(bt, True)
+    b = gpu_plan(bt, True)
+    T = a[4]["T"]
+    assert T == b[4]["T"]
+    for f in ("src", "seg_start"):     # capacity B*S; the first T entries are defined
+        assert torch.equal(getattr(a[4].plan, f)[:T], getattr(b[4].plan, f)[:T])
+    for f in ("dst", "resp_off", "resp_len", "group_of", "grp_idx"):
+        assert torch.equal(getattr(a[4].plan, f), getattr(b[4].plan, f))
