@@ -41,6 +41,10 @@ SMALL = {
                                   num_q_heads=8, num_kv_heads=1, head_dim=64, dtype="bf16", sigma=0.5, seed=36),
     "bf16_gqa3": _base.scaled(name="bf16_gqa3", num_prompts=2, rollout_n=2, prompt_len=70, response_len=30,
                               num_q_heads=3, num_kv_heads=1, head_dim=128, dtype="bf16", sigma=0.5, seed=37),
+    # mid-size, every element compared: 2 prompts x 4 responses, prompt 2048, response 512, GQA 16/8/128
+    "bf16_mid_2x4_p2048_r512": _base.scaled(name="bf16_mid_2x4_p2048_r512", num_prompts=2, rollout_n=4,
+                                            prompt_len=2048, response_len=512, num_q_heads=16, num_kv_heads=8,
+                                            head_dim=128, dtype="bf16", sigma=0.5, vocab=151936, seed=39),
     "bf16_unit_sigma": _base.scaled(name="bf16_unit_sigma", num_prompts=2, rollout_n=4, prompt_len=256,
                                     response_len=64, num_q_heads=4, num_kv_heads=2, head_dim=128, dtype="bf16",
                                     sigma=1.0, seed=38),
@@ -166,7 +170,7 @@ def _sample_rows(info, rng, n_random=6):
 def test_full_forward_sampled(full):
     c, name = full, full["name"]
     w, info, x = c["w"], c["oinfo"], c["x"]
-    rows = _sample_rows(info, np.random.default_rng(1))
+    rows = _sample_rows(info, np.random.default_rng(1), n_random=48)
     heads = [0, w.num_q_heads - 1]
     say(f"[attn full] {name}: forward on {len(rows)} rows x {len(heads)} heads")
     ro, rl = oracle.forward_rows(x["q"], x["k"], x["v"], info, rows, heads)
@@ -180,7 +184,7 @@ def test_full_backward_sampled(full):
     c, name = full, full["name"]
     w, info, x = c["w"], c["oinfo"], c["x"]
     rng = np.random.default_rng(2)
-    rows = _sample_rows(info, rng, n_random=4)
+    rows = _sample_rows(info, rng, n_random=40)
     heads = [1, w.num_q_heads - 2]
     say(f"[attn full] {name}: dq on {len(rows)} rows")
     rdq = oracle.dq_rows(x["q"], x["k"], x["v"], x["do"], info, rows, heads)
