@@ -36,7 +36,6 @@ constexpr float kNeg = -1.0e30f;      // score of a key a row does not see
 constexpr float kVisibleFloor = -1.0e29f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 __device__ inline f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -100,125 +99,8 @@ __device__ inline void stage_rows_t(char *dst, const __bf16 *src, int r0, int T,
   }
 }
 
-// ---------------------------------------------------------------------------
-// Forward
-// ---------------------------------------------------------------------------
-
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kBN = 64;         // keys per LDS tile
-
-template <int D, int HPW>
-__global__ void __launch_bounds__(kThreads) k_fwd_bf16(const Tile *__restrict__ tiles, const int *__restrict__ ntiles,
-                                                       int HG, int Hq, int Hkv, int T, const __bf16 *__restrict__ q,
-                                                       const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
-                                                       __bf16 *__restrict__ o, float *__restrict__ lse,
-                                                       const int *__restrict__ seg_start, float scale_log2) {
-  constexpr int WPH = 4 / HPW;        // waves per head
-  constexpr int KS = D / 16;          // contraction steps over head_dim
-  constexpr int KSTR = D * 2 + 16;    // K tile row stride (bytes)
-  constexpr int VSTR = kBN * 2 + 16;  // V^T tile row stride (bytes)
-  __shared__ __attribute__((aligned(16))) char smem[kBN * KSTR + D * VSTR];
-  char *Ks = smem;
-  char *Vt = smem + kBN * KSTR;
-
-  const int tile_rank = blockIdx.x / HG;
-  if (tile_rank >= *ntiles) return;
-  const int hg = blockIdx.x % HG;
-  const int ratio = Hq / Hkv;
-  const int sub = ratio / HPW;
-  const int kvh = hg / sub;
-  const Tile t = tiles[tile_rank];
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int half = lane >> 5, col = lane & 31;
-  const int h = kvh * ratio + (hg % sub) * HPW + wave / WPH;
-  const int qrow = t.r0 + (wave % WPH) * 32 + col;
-  const bool qvalid = qrow < t.r1;
-  const int seg_q = qvalid ? seg_start[qrow] : 0x7fffffff;
-
-  bf16x8 qf[KS];
-  {
-    const __bf16 *qp = q + (int64_t(qvalid ? qrow : t.r0) * Hq + h) * D + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = qvalid ? ld8(qp + 16 * ks) : zero8();
-  }
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
-  float m_run = kNeg, l_run = 0.0f;
-
-  auto process = [&](int kt, bool prompt_keys, int klim) {
-    __syncthreads();
-    stage_rows<kBN, D, KSTR, kThreads>(Ks, k, kt, T, Hkv, kvh);
-    stage_rows_t<kBN, D, VSTR, kThreads>(Vt, v, kt, T, Hkv, kvh);
-    __syncthreads();
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
-      const char *ap = Ks + (32 * kb + col) * KSTR + 16 * half;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[kb] = mfma(lds8(ap + 32 * ks), qf[ks], s[kb]);
-    }
-    float mt = kNeg;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt + 32 * kb + c_row(r, half);
-        const bool vis = prompt_keys ? (key < klim) : (key <= qrow && key >= seg_q);
-        const float x = vis ? s[kb][r] * scale_log2 : kNeg;
-        s[kb][r] = x;
-        mt = fmaxf(mt, x);
-      }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - mn);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-      m_run = mn;
-    }
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = s[kb][r];
-        const float p = x > kVisibleFloor ? exp2f(x - m_run) : 0.0f;
-        l_run += p;
-        pf[2 * kb + (r >> 3)][r & 7] = static_cast<__bf16>(p);
-      }
-    }
-#pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk) {
-      const char *ap = Vt + (32 * dblk + col) * VSTR + 16 * half;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) oacc[dblk] = mfma(lds8(ap + 32 * ks), pf[ks], oacc[dblk]);
-    }
-  };
-
-  for (int kt = t.u0; kt < t.u1; kt += kBN) process(kt, true, t.u1);
-  for (int kt = t.s0; kt < t.r1; kt += kBN) process(kt, false, 0);
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qvalid) {
-    const float inv = 1.0f / l_tot;
-    __bf16 *op = o + (int64_t(qrow) * Hq + h) * D;
-#pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        bf16x4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = static_cast<__bf16>(oacc[dblk][4 * rg + i] * inv);
-        *reinterpret_cast<bf16x4 *>(op + 32 * dblk + 8 * rg + 4 * half) = w;
-      }
-    }
-    if (half == 0) lse[int64_t(h) * T + qrow] = (m_run + log2f(l_tot)) * kLn2;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Backward preprocess: Dbuf[h, row] = sum_d dO[row, h, d] O[row, h, d]
@@ -482,7 +364,6 @@ int heads_per_block(const spd_attn_desc &d) {
 
 }  // namespace
 
-int fwd_bf16_rows_per_tile(const spd_attn_desc &d) { return 32 * (4 / heads_per_block(d)); }
 int dq_bf16_rows_per_tile(const spd_attn_desc &d) { return 32 * (4 / heads_per_block(d)); }
 int dkdv_bf16_rows_per_tile(const spd_attn_desc &) { return 128; }
 
@@ -492,32 +373,6 @@ int dkdv_bf16_rows_per_tile(const spd_attn_desc &) { return 128; }
     case 2: { constexpr int HPW = 2; __VA_ARGS__; } break; \
     default: { constexpr int HPW = 1; __VA_ARGS__; } break; \
   }
-
-spd_status attn_fwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *tiles,
-                         const int *ntiles, int64_t cap, const void *q, const void *k, const void *v, void *o,
-                         float *lse, hipStream_t st) {
-  const int hpw = heads_per_block(d);
-  const int HG = d.num_q_heads / hpw;
-  const dim3 grid(static_cast<unsigned>(cap * HG));
-  const float sl2 = d.softmax_scale * kLog2e;
-  const auto *qq = static_cast<const __bf16 *>(q);
-  const auto *kk = static_cast<const __bf16 *>(k);
-  const auto *vv = static_cast<const __bf16 *>(v);
-  auto *oo = static_cast<__bf16 *>(o);
-  prof_start(SPD_K_FWD, st);
-  if (d.head_dim == 128) {
-    SPD_DISPATCH_HPW(hpw, hipLaunchKernelGGL((k_fwd_bf16<128, HPW>), grid, dim3(kThreads), 0, st, tiles, ntiles, HG,
-                                             d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv, oo, lse,
-                                             plan.seg_start, sl2));
-  } else {
-    SPD_DISPATCH_HPW(hpw, hipLaunchKernelGGL((k_fwd_bf16<64, HPW>), grid, dim3(kThreads), 0, st, tiles, ntiles, HG,
-                                             d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv, oo, lse,
-                                             plan.seg_start, sl2));
-  }
-  SPD_LAUNCH_CHECK();
-  prof_stop(SPD_K_FWD, st);
-  return SPD_OK;
-}
 
 spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *qtiles, const int *nq,
                          int64_t capq, const Tile *ktiles, const int *nk, int64_t capk, const void *q, const void *k,

@@ -1,0 +1,109 @@
+// Device building blocks shared by the bf16 split-attention kernels (gfx950).
+//
+// Matrix core: v_mfma_f32_32x32x16_bf16 (wave64).  Lane l supplies row
+// (l % 32) of A and column (l % 32) of B as 8 bf16 along the contraction; the
+// fp32 result holds C[8 (r / 4) + 4 (l / 32) + (r % 4)][l % 32] in register r.
+// Only the pairing of A and B contraction slots matters, so an operand may list
+// its 8 contraction indices in any order as long as the other operand lists
+// the same ones.  A result reused as an operand (probabilities, dS) therefore
+// lists, in lane half h, the rows {4h..4h+3, 8+4h..8+4h+3} of each 16-row step.
+//
+// Tiles live in LDS row-major with 16-byte chunks XOR-swizzled by row (slot =
+// chunk ^ (row mod chunks-per-row)), which keeps a half-wave's 16-byte reads of
+// one column on distinct banks.  They are filled with direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l), so no
+// registers or ALU time are spent staging them.
+//
+// The transposed operands (V^T, K^T, Q^T, dO^T) are read straight from those
+// row-major tiles with ds_read_b64_tr_b16: in each 16-lane group, output lane
+// i, element j is element (i % 4) of the 8 bytes read by lane 4 j + i / 4.
+// If lane s of the group reads row key(s / 4), columns c0 + 4 (s % 4) ... + 3,
+// output lane i holds column c0 + i of rows key(0..3): the column-major slice
+// an MFMA operand needs, with the 4 rows free to choose.
+#pragma once
+
+#include "spd_attn.h"
+
+namespace spd {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ inline f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+__device__ inline bf16x8 zero8() {
+  return __builtin_bit_cast(bf16x8, i16x8{0, 0, 0, 0, 0, 0, 0, 0});
+}
+
+__device__ inline bf16x8 ld_global8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ inline bf16x8 ld_lds8(const char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// Two transposing 8-byte LDS reads concatenated into one MFMA operand.
+__device__ inline bf16x8 ld_lds_tr_pair(const char *p0, const char *p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p1));
+  const i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Row (0..31) of register r of a 32x32 result for lane half h.
+__device__ inline int c_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Byte offset of 16-byte chunk `chunk` of row `row` in a swizzled tile of D columns.
+template <int D>
+__device__ inline int swz_off(int row, int chunk) {
+  constexpr int CPR = D / 8;
+  return row * (D * 2) + ((chunk ^ (row & (CPR - 1))) << 4);
+}
+
+// Direct-to-LDS copy of rows [r0, r0 + ROWS) of a [*, H, D] bf16 tensor (head
+// hh) into a swizzled tile, spread over NW waves.  Rows past T - 1 are clamped
+// to T - 1: they hold real (finite) data and every consumer masks them.
+template <int ROWS, int D, int NW>
+__device__ inline void dma_rows(char *tile, const __bf16 *src, int r0, int T, int H, int hh, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int CHUNKS = ROWS * CPR;
+  static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
+  constexpr int PER_WAVE = CHUNKS / (NW * 64);
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int blk = wave * PER_WAVE + i;
+    const int L = blk * 64 + lane;
+    const int r = L / CPR;
+    const int slot = L % CPR;
+    const int chunk = slot ^ (r & (CPR - 1));
+    const int row = min(r0 + r, T - 1);
+    const char *g = reinterpret_cast<const char *>(src + (int64_t(row) * H + hh) * D) + (chunk << 4);
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)(tile + blk * 1024), 16, 0, 0);
+  }
+}
+
+// Waits for this wave's outstanding memory operations (direct-to-LDS loads
+// included), then for every wave of the block.
+__device__ inline void wait_tile() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+}  // namespace dev
+}  // namespace spd
