@@ -59,7 +59,12 @@ spd_status attn_fwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
 spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *qtiles,
                          const int *nq, int64_t capq, const Tile *ktiles, const int *nk, int64_t capk,
                          const void *q, const void *k, const void *v, const void *o, const float *lse,
-                         const void *dout, void *dq, void *dk, void *dv, float *Dbuf, hipStream_t st);
+                         const void *dout, void *dq, void *dk, void *dv, float *Dbuf, float *L2buf, int *segp,
+                         int64_t Tp, hipStream_t st);
+
+// Row stride of the backward's per-row scalar arrays: T rounded up to 64, plus
+// one 64-row block, so that 64-row reads starting below T stay inside.
+inline int64_t padded_rows(int64_t T) { return (T + 63) / 64 * 64 + 64; }
 
 // Rows per tile of the fp32 kernels.
 constexpr int kF32Rows = 64;

@@ -122,8 +122,9 @@ namespace {
 struct AttnWs {
   Tile *qtiles = nullptr, *ktiles = nullptr, *tmp = nullptr;
   int *counts = nullptr;
-  float *Dbuf = nullptr;
-  int64_t capq = 0, capk = 0;
+  float *Dbuf = nullptr, *L2buf = nullptr;
+  int *segp = nullptr;
+  int64_t capq = 0, capk = 0, Tp = 0;
   size_t bytes = 0;
 };
 
@@ -131,13 +132,16 @@ int q_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : fwd_
 int dq_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dq_bf16_rows_per_tile(d); }
 int k_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dkdv_bf16_rows_per_tile(d); }
 
-// Workspace: [D: Hq*T floats][query tiles][key tiles][scratch tiles][counts]
+// Workspace: [D: Hq*Tp floats][log2 LSE: Hq*Tp floats][seg_start copy: Tp ints]
+//            [query tiles][key tiles][scratch tiles][counts]
 AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
   AttnWs w;
   const int rq = std::min(q_rows(d), dq_rows(d));
   w.capq = tile_capacity(B, T, rq);
   w.capk = tile_capacity(B, T, k_rows(d));
-  const size_t dbytes = round_up(size_t(d.num_q_heads) * size_t(T) * 4, 256);
+  w.Tp = padded_rows(T);
+  const size_t dbytes = round_up(size_t(d.num_q_heads) * size_t(w.Tp) * 4, 256);
+  const size_t sbytes = round_up(size_t(w.Tp) * 4, 256);
   const size_t qb = round_up(size_t(w.capq) * sizeof(Tile), 256);
   const size_t kb = round_up(size_t(w.capk) * sizeof(Tile), 256);
   const size_t tb = std::max(qb, kb);
@@ -145,6 +149,10 @@ AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
   size_t off = 0;
   if (p) w.Dbuf = reinterpret_cast<float *>(p + off);
   off += dbytes;
+  if (p) w.L2buf = reinterpret_cast<float *>(p + off);
+  off += dbytes;
+  if (p) w.segp = reinterpret_cast<int *>(p + off);
+  off += sbytes;
   if (p) w.qtiles = reinterpret_cast<Tile *>(p + off);
   off += qb;
   if (p) w.ktiles = reinterpret_cast<Tile *>(p + off);
@@ -223,5 +231,5 @@ extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_pl
                         static_cast<const float *>(o), lse, static_cast<const float *>(dout),
                         static_cast<float *>(dq), static_cast<float *>(dk), static_cast<float *>(dv), w.Dbuf, st);
   return attn_bwd_bf16(*desc, *plan, T, w.qtiles, w.counts, w.capq, w.ktiles, w.counts + 1, w.capk, q, k, v, o, lse,
-                       dout, dq, dk, dv, w.Dbuf, st);
+                       dout, dq, dk, dv, w.Dbuf, w.L2buf, w.segp, w.Tp, st);
 }

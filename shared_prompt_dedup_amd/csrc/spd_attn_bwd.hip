@@ -1,0 +1,465 @@
+// bf16 split-attention backward on CDNA4 matrix cores.
+//
+// How Prompt Deduplication Works -- "Correctness & Gradients": gradients
+// flow through the deduplicated computation.  With P = softmax(scale S),
+// D = rowsum(dO * O), dP = dO V^T, dS = P (dP - D):
+//   dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dO.
+// A prompt key's dk / dv sum over the prompt's own causal queries and over
+// every response row of its group; query heads sharing a kv head add into it.
+//
+// k_bwd_pre: D and the log2-scaled LSE per (head, row).
+// k_dq: one block per query tile (as the forward), K and V tiles by
+//   direct-to-LDS loads, S^T = K Q^T, dP^T = V dO^T, dq^T += K^T dS^T with
+//   K^T read by transposing LDS reads.
+// k_dkdv: one block per 128-key tile and kv head; 8 waves = 4 blocks of 32
+//   keys x 2 query-row parities.  K and V of a wave's keys stay in registers;
+//   Q and dO tiles of 64 query rows (plus their LSE, D and segment starts)
+//   arrive by direct-to-LDS loads, double buffered.  S = Q K^T and
+//   dP = dO V^T put one key per lane column, so P^T and dS^T feed
+//   dv += P^T dO and dk += dS^T Q directly, with dO^T and Q^T read by
+//   transposing LDS reads.  The two parity waves of a key block add their
+//   partial sums through LDS in a fixed order.  No atomics anywhere: results
+//   are bitwise repeatable.
+#include "spd_attn_dev.h"
+
+namespace spd {
+namespace {
+
+using namespace dev;
+
+constexpr int kWaves = 8;
+constexpr int kBN = 64;      // keys per tile in k_dq
+constexpr int kQB = 64;      // query rows per staged block in k_dkdv
+
+// D[h, row] = sum_d dO[row, h, d] O[row, h, d];  L2[h, row] = lse[h, row] log2(e);
+// segp[row] = seg_start[row].  The three arrays have a row stride of Tp >= T + 64
+// so that 64-row blocks starting below T never leave them; the padding rows
+// are set to 0 and are masked by every reader.
+template <int D>
+__global__ void __launch_bounds__(256) k_bwd_pre(int64_t rows_x_heads, int Hq, int T, int Tp,
+                                                 const __bf16 *__restrict__ o, const __bf16 *__restrict__ dout,
+                                                 const float *__restrict__ lse, const int *__restrict__ seg_start,
+                                                 float *__restrict__ Dbuf, float *__restrict__ L2buf,
+                                                 int *__restrict__ segp) {
+  constexpr int LPR = D / 8;     // lanes per (row, head)
+  constexpr int RPW = 64 / LPR;  // (row, head) pairs per wave
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t i = wave * RPW + lane / LPR;
+  const int sub = lane % LPR;
+  float s = 0.0f;
+  if (i < rows_x_heads) {
+    const bf16x8 a = ld_global8(o + i * D + sub * 8);
+    const bf16x8 b = ld_global8(dout + i * D + sub * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(static_cast<float>(a[e]), static_cast<float>(b[e]), s);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (i < rows_x_heads && sub == 0) {
+    const int64_t row = i / Hq;
+    const int h = static_cast<int>(i % Hq);
+    const int64_t at = int64_t(h) * Tp + row;
+    Dbuf[at] = s;
+    L2buf[at] = lse[int64_t(h) * T + row] * kLog2e;
+    if (h == 0) segp[row] = seg_start[row];
+  }
+  // zero the padding rows [T, Tp) of every array
+  const int64_t pad = int64_t(Tp - T) * (Hq + 1);
+  const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t nthreads = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t j = tid; j < pad; j += nthreads) {
+    const int64_t a = j / (Tp - T), r = T + j % (Tp - T);
+    if (a < Hq) {
+      Dbuf[a * Tp + r] = 0.0f;
+      L2buf[a * Tp + r] = 0.0f;
+    } else {
+      segp[r] = 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- dq
+
+template <int D, int HPW>
+__global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ tiles, const int *__restrict__ ntiles,
+                                                    int HG, int Hq, int Hkv, int T, const __bf16 *__restrict__ q,
+                                                    const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+                                                    const float *__restrict__ L2buf,
+                                                    const __bf16 *__restrict__ dout, const float *__restrict__ Dbuf,
+                                                    int Tp, __bf16 *__restrict__ dq,
+                                                    const int *__restrict__ seg_start, float scale_log2,
+                                                    float scale) {
+  constexpr int NW = kWaves, BN = kBN;
+  constexpr int WPH = NW / HPW;
+  constexpr int KS = D / 16;
+  constexpr int TB = BN * D * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];   // [stage][K | V]
+
+  const int tile_rank = blockIdx.x / HG;
+  if (tile_rank >= *ntiles) return;
+  const int hg = blockIdx.x % HG;
+  const int ratio = Hq / Hkv;
+  const int sub = ratio / HPW;
+  const int kvh = hg / sub;
+  const Tile t = tiles[tile_rank];
+  const int wave = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, col = lane & 31;
+  const int h = kvh * ratio + (hg % sub) * HPW + wave / WPH;
+  const int qw0 = t.r0 + (wave % WPH) * 32;
+  const int qlast = min(t.r1, qw0 + 32) - 1;
+  const int qrow = qw0 + col;
+  const bool qvalid = qrow < t.r1;
+  const int seg_q = qvalid ? seg_start[qrow] : 0x7fffffff;
+  const int seg_hi = qlast >= qw0 ? seg_start[qlast] : 0x7fffffff;
+  const float lse2 = qvalid ? L2buf[int64_t(h) * Tp + qrow] : 0.0f;
+  const float Dq = qvalid ? Dbuf[int64_t(h) * Tp + qrow] : 0.0f;
+
+  bf16x8 qf[KS], df[KS];
+  {
+    const int64_t off = (int64_t(qvalid ? qrow : t.r0) * Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = qvalid ? ld_global8(q + off + 16 * ks) : zero8();
+      df[ks] = qvalid ? ld_global8(dout + off + 16 * ks) : zero8();
+    }
+  }
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = zero16();
+
+  int roff[KS];   // row reads of K / V: row 32 kb + col, chunk 2 ks + half
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = swz_off<D>(col, 2 * ks + half);
+  const int grp = lane >> 4, s16 = lane & 15;
+  int toff[D / 32][2];   // K^T reads (transposing)
+#pragma unroll
+  for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int row = 8 * w + 4 * (grp >> 1) + (s16 >> 2);
+      const int dcol = 32 * dblk + 16 * (grp & 1) + 4 * (s16 & 3);
+      toff[dblk][w] = swz_off<D>(row, dcol >> 3) + ((dcol & 7) << 1);
+    }
+
+  const int nA = (t.u1 - t.u0 + BN - 1) / BN;
+  const int nB = (t.r1 - t.s0 + BN - 1) / BN;
+  const int n = nA + nB;
+  auto kt_of = [&](int i) { return i < nA ? t.u0 + i * BN : t.s0 + (i - nA) * BN; };
+
+  dma_rows<BN, D, NW>(smem, k, kt_of(0), T, Hkv, kvh, wave, lane);
+  dma_rows<BN, D, NW>(smem + TB, v, kt_of(0), T, Hkv, kvh, wave, lane);
+
+  for (int i = 0; i < n; ++i) {
+    wait_tile();
+    if (i + 1 < n) {
+      char *nxt = smem + ((i + 1) & 1) * 2 * TB;
+      dma_rows<BN, D, NW>(nxt, k, kt_of(i + 1), T, Hkv, kvh, wave, lane);
+      dma_rows<BN, D, NW>(nxt + TB, v, kt_of(i + 1), T, Hkv, kvh, wave, lane);
+    }
+    const int kt = kt_of(i);
+    const bool phaseA = i < nA;
+    if (qlast < qw0 || (!phaseA && kt > qlast)) continue;
+    const char *Ks = smem + (i & 1) * 2 * TB;
+    const char *Vs = Ks + TB;
+    const bool need_mask = phaseA ? (kt + BN > t.u1) : (kt + BN - 1 > qw0 || kt < seg_hi);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma(ld_lds8(Ks + roff[ks] + kb * 32 * D * 2), qf[ks], s);
+        dp = mfma(ld_lds8(Vs + roff[ks] + kb * 32 * D * 2), df[ks], dp);
+      }
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -lse2));
+        if (need_mask) {
+          const int key = kt + 32 * kb + c_row(r, half);
+          const bool vis = phaseA ? (key < t.u1) : (key <= qrow && key >= seg_q);
+          p = vis ? p : 0.0f;
+        }
+        dsf[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - Dq));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ks = 2 * kb + j;
+#pragma unroll
+        for (int dblk = 0; dblk < D / 32; ++dblk) {
+          const bf16x8 a = ld_lds_tr_pair(Ks + toff[dblk][0] + ks * 16 * D * 2, Ks + toff[dblk][1] + ks * 16 * D * 2);
+          acc[dblk] = mfma(a, dsf[j], acc[dblk]);
+        }
+      }
+    }
+  }
+
+  if (qvalid) {
+    __bf16 *op = dq + (int64_t(qrow) * Hq + h) * D;
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = static_cast<__bf16>(acc[dblk][4 * rg + e] * scale);
+        *reinterpret_cast<bf16x4 *>(op + 32 * dblk + 8 * rg + 4 * half) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------- dk / dv
+
+// Direct-to-LDS copy of the per-row scalars of query rows [r0, r0 + 64) of
+// head h: log2-LSE, D (float, row stride Tp) and seg_start (int).  One wave,
+// lanes 0..47 (16 lanes x 16 bytes per array); r0 < T and Tp >= T + 64 keep
+// every read inside the padded arrays.
+__device__ inline void dma_row_scalars(char *dst, const float *L2buf, const float *Dbuf, const int *segp, int r0,
+                                       int Tp, int h, int lane) {
+  if (lane < 48) {
+    const int arr = lane >> 4, part = lane & 15;
+    const int64_t at = int64_t(h) * Tp + r0 + 4 * part;
+    const void *g = arr == 0 ? static_cast<const void *>(L2buf + at)
+                             : arr == 1 ? static_cast<const void *>(Dbuf + at)
+                                        : static_cast<const void *>(segp + r0 + 4 * part);
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)(dst), 16, 0, 0);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ tiles, const int *__restrict__ ntiles,
+                                                      int Hq, int Hkv, int T, const __bf16 *__restrict__ q,
+                                                      const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+                                                      const float *__restrict__ L2buf,
+                                                      const __bf16 *__restrict__ dout,
+                                                      const float *__restrict__ Dbuf,
+                                                      const int *__restrict__ segp, int Tp, __bf16 *__restrict__ dk,
+                                                      __bf16 *__restrict__ dv, float scale_log2, float scale) {
+  constexpr int NW = kWaves, QB = kQB;
+  constexpr int KS = D / 16;
+  constexpr int TB = QB * D * 2;                    // one Q or dO tile
+  constexpr int SB = 3 * QB * 4;                    // LSE2 | D | seg_start of the block
+  constexpr int STAGE = 2 * TB + 1024;              // Q | dO | scalars (padded)
+  constexpr int XB = 4 * 32 * D * 4;                // one exchange round: 4 key blocks x 32 keys x D floats
+  constexpr int SMEM = (2 * STAGE > XB) ? 2 * STAGE : XB;
+  static_assert(SB <= 1024, "row scalars fit their slot");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int tile_rank = blockIdx.x / Hkv;
+  if (tile_rank >= *ntiles) return;
+  const int kvh = blockIdx.x % Hkv;
+  const Tile t = tiles[tile_rank];
+  const int wave = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, col = lane & 31;
+  const int kblk = wave & 3, par = wave >> 2;
+  const int key = t.r0 + 32 * kblk + col;   // this lane's key column
+  const bool kvalid = key < t.r1;
+  const int ratio = Hq / Hkv;
+
+  bf16x8 kf[KS], vf[KS];
+  {
+    const int64_t off = (int64_t(kvalid ? key : t.r0) * Hkv + kvh) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = kvalid ? ld_global8(k + off + 16 * ks) : zero8();
+      vf[ks] = kvalid ? ld_global8(v + off + 16 * ks) : zero8();
+    }
+  }
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dka[i] = zero16();
+    dva[i] = zero16();
+  }
+
+  // This wave's 32 query rows of a staged block: rows 32 par .. 32 par + 31.
+  int roff[KS];   // row reads of Q / dO (A operands): row 32 par + col, chunk 2 ks + half
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = swz_off<D>(32 * par + col, 2 * ks + half);
+  const int grp = lane >> 4, s16 = lane & 15;
+  int toff[D / 32][2];   // dO^T / Q^T reads: rows 32 par + 16 ks + 8 w + 4 (grp/2) + s16/4
+#pragma unroll
+  for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int row = 32 * par + 8 * w + 4 * (grp >> 1) + (s16 >> 2);
+      const int dcol = 32 * dblk + 16 * (grp & 1) + 4 * (s16 & 3);
+      toff[dblk][w] = swz_off<D>(row, dcol >> 3) + ((dcol & 7) << 1);
+    }
+
+  const int nA = (t.u1 - t.u0 + QB - 1) / QB;   // masked query rows
+  const int nB = (t.e0 - t.s0 + QB - 1) / QB;   // unmasked query rows
+  const int nper = nA + nB;
+  const int n = nper * ratio;
+  auto blk_of = [&](int i, int &h, int &qb, bool &masked, int &qend) {
+    const int hh = i / nper, j = i % nper;
+    h = kvh * ratio + hh;
+    masked = j < nA;
+    qb = masked ? t.u0 + j * QB : t.s0 + (j - nA) * QB;
+    qend = masked ? t.u1 : t.e0;
+  };
+  auto issue = [&](int i, char *st) {
+    int h, qb, qend;
+    bool masked;
+    blk_of(i, h, qb, masked, qend);
+    dma_rows<QB, D, NW>(st, q, qb, T, Hq, h, wave, lane);
+    dma_rows<QB, D, NW>(st + TB, dout, qb, T, Hq, h, wave, lane);
+    if (wave == 0) dma_row_scalars(st + 2 * TB, L2buf, Dbuf, segp, qb, Tp, h, lane);
+  };
+
+  if (n > 0) issue(0, smem);
+  for (int i = 0; i < n; ++i) {
+    wait_tile();
+    if (i + 1 < n) issue(i + 1, smem + ((i + 1) & 1) * STAGE);
+    int h, qb, qend;
+    bool masked;
+    blk_of(i, h, qb, masked, qend);
+    const int row0 = qb + 32 * par;                 // first query row of this wave
+    const int kmin = t.r0 + 32 * kblk;              // smallest key of this wave
+    if (row0 >= qend) continue;                     // no rows
+    if (masked && row0 + 31 < kmin) continue;       // every row precedes every key
+    const char *Qs = smem + (i & 1) * STAGE;
+    const char *Ds = Qs + TB;
+    const float *sL2 = reinterpret_cast<const float *>(Qs + 2 * TB);        // entry e = row qb + e
+    const float *sD = reinterpret_cast<const float *>(Qs + 2 * TB + 256);
+    const int *sSeg = reinterpret_cast<const int *>(Qs + 2 * TB + 512);
+
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma(ld_lds8(Qs + roff[ks]), kf[ks], s);
+      dp = mfma(ld_lds8(Ds + roff[ks]), vf[ks], dp);
+    }
+    bf16x8 pf[2], dsf[2];
+    const bool need_mask = masked || row0 + 31 >= qend;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = 32 * par + c_row(r, half);       // entry in the block's scalar arrays
+      const int row = qb + e;
+      float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -sL2[e]));
+      float ds = p * (dp[r] - sD[e]);
+      if (need_mask) {
+        bool vis = row < qend;
+        if (masked) vis = vis && key <= row && key >= sSeg[e];
+        p = vis ? p : 0.0f;
+        ds = vis ? ds : 0.0f;
+      }
+      pf[r >> 3][r & 7] = static_cast<__bf16>(p);
+      dsf[r >> 3][r & 7] = static_cast<__bf16>(ds);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int dblk = 0; dblk < D / 32; ++dblk) {
+        const bf16x8 bdo = ld_lds_tr_pair(Ds + toff[dblk][0] + j * 16 * D * 2, Ds + toff[dblk][1] + j * 16 * D * 2);
+        const bf16x8 bq = ld_lds_tr_pair(Qs + toff[dblk][0] + j * 16 * D * 2, Qs + toff[dblk][1] + j * 16 * D * 2);
+        dva[dblk] = mfma(pf[j], bdo, dva[dblk]);
+        dka[dblk] = mfma(dsf[j], bq, dka[dblk]);
+      }
+  }
+
+  // Combine the two parities of each key block through LDS, in a fixed order:
+  // round 1 parity 1 hands its dk partial to parity 0, which writes dk;
+  // round 2 parity 0 hands its dv partial to parity 1, which writes dv.
+  float *xch = reinterpret_cast<float *>(smem);
+  const int xbase = kblk * 32 * D;   // floats
+  auto put = [&](const f32x16 *a) {
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[xbase + c_row(r, half) * D + 32 * dblk + col] = a[dblk][r];
+  };
+  auto take_and_store = [&](const f32x16 *a, __bf16 *out, float mul) {
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = c_row(r, half);
+        const float val = (a[dblk][r] + xch[xbase + kr * D + 32 * dblk + col]) * mul;
+        const int kk = t.r0 + 32 * kblk + kr;
+        if (kk < t.r1) out[(int64_t(kk) * Hkv + kvh) * D + 32 * dblk + col] = static_cast<__bf16>(val);
+      }
+  };
+  wait_tile();
+  if (par == 1) put(dka);
+  __syncthreads();
+  if (par == 0) take_and_store(dka, dk, scale);
+  __syncthreads();
+  if (par == 0) put(dva);
+  __syncthreads();
+  if (par == 1) take_and_store(dva, dv, 1.0f);
+}
+
+int bwd_heads_per_block(const spd_attn_desc &d) {
+  const int ratio = d.num_q_heads / d.num_kv_heads;
+  return (ratio % 4 == 0) ? 4 : (ratio % 2 == 0 ? 2 : 1);
+}
+
+}  // namespace
+
+int dq_bf16_rows_per_tile(const spd_attn_desc &d) { return 32 * (kWaves / bwd_heads_per_block(d)); }
+int dkdv_bf16_rows_per_tile(const spd_attn_desc &) { return 128; }
+
+spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *qtiles, const int *nq,
+                         int64_t capq, const Tile *ktiles, const int *nk, int64_t capk, const void *q, const void *k,
+                         const void *v, const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                         void *dv, float *Dbuf, float *L2buf, int *segp, int64_t Tp, hipStream_t st) {
+  const auto *qq = static_cast<const __bf16 *>(q);
+  const auto *kk = static_cast<const __bf16 *>(k);
+  const auto *vv = static_cast<const __bf16 *>(v);
+  const auto *oo = static_cast<const __bf16 *>(o);
+  const auto *dd = static_cast<const __bf16 *>(dout);
+  const int64_t n = T * d.num_q_heads;
+  const int rpw = 64 / (d.head_dim / 8);
+  const int64_t waves = (n + rpw - 1) / rpw;
+  const dim3 gpre(static_cast<unsigned>((waves + 3) / 4));
+  prof_start(SPD_K_BWD_PRE, st);
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL(k_bwd_pre<128>, gpre, dim3(256), 0, st, n, d.num_q_heads, int(T), int(Tp), oo, dd, lse,
+                       plan.seg_start, Dbuf, L2buf, segp);
+  else
+    hipLaunchKernelGGL(k_bwd_pre<64>, gpre, dim3(256), 0, st, n, d.num_q_heads, int(T), int(Tp), oo, dd, lse,
+                       plan.seg_start, Dbuf, L2buf, segp);
+  SPD_LAUNCH_CHECK();
+  prof_stop(SPD_K_BWD_PRE, st);
+
+  const int hpw = bwd_heads_per_block(d);
+  const int HG = d.num_q_heads / hpw;
+  const float sl2 = d.softmax_scale * kLog2e;
+  const dim3 block(kWaves * 64);
+  const dim3 gq(static_cast<unsigned>(capq * HG));
+  const dim3 gk(static_cast<unsigned>(capk * d.num_kv_heads));
+  auto *dqq = static_cast<__bf16 *>(dq);
+  auto *dkk = static_cast<__bf16 *>(dk);
+  auto *dvv = static_cast<__bf16 *>(dv);
+  prof_start(SPD_K_BWD_DQ, st);
+#define SPD_DQ_LAUNCH(DD, HH)                                                                                     \
+  hipLaunchKernelGGL((k_dq<DD, HH>), gq, block, 0, st, qtiles, nq, HG, d.num_q_heads, d.num_kv_heads, int(T), qq, \
+                     kk, vv, L2buf, dd, Dbuf, int(Tp), dqq, plan.seg_start, sl2, d.softmax_scale)
+  if (d.head_dim == 128) {
+    if (hpw == 4) SPD_DQ_LAUNCH(128, 4);
+    else if (hpw == 2) SPD_DQ_LAUNCH(128, 2);
+    else SPD_DQ_LAUNCH(128, 1);
+  } else {
+    if (hpw == 4) SPD_DQ_LAUNCH(64, 4);
+    else if (hpw == 2) SPD_DQ_LAUNCH(64, 2);
+    else SPD_DQ_LAUNCH(64, 1);
+  }
+#undef SPD_DQ_LAUNCH
+  SPD_LAUNCH_CHECK();
+  prof_stop(SPD_K_BWD_DQ, st);
+  prof_start(SPD_K_BWD_DKDV, st);
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL(k_dkdv<128>, gk, block, 0, st, ktiles, nk, d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv,
+                       L2buf, dd, Dbuf, segp, int(Tp), dkk, dvv, sl2, d.softmax_scale);
+  else
+    hipLaunchKernelGGL(k_dkdv<64>, gk, block, 0, st, ktiles, nk, d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv,
+                       L2buf, dd, Dbuf, segp, int(Tp), dkk, dvv, sl2, d.softmax_scale);
+  SPD_LAUNCH_CHECK();
+  prof_stop(SPD_K_BWD_DKDV, st);
+  return SPD_OK;
+}
+
+}  // namespace spd
