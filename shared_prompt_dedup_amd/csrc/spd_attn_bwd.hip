@@ -11,15 +11,14 @@
 // k_dq: one block per query tile (as the forward), K and V tiles by
 //   direct-to-LDS loads, S^T = K Q^T, dP^T = V dO^T, dq^T += K^T dS^T with
 //   K^T read by transposing LDS reads.
-// k_dkdv: one block per 128-key tile and kv head; 8 waves = 4 blocks of 32
-//   keys x 2 query-row parities.  K and V of a wave's keys stay in registers;
-//   Q and dO tiles of 64 query rows (plus their LSE, D and segment starts)
-//   arrive by direct-to-LDS loads, double buffered.  S = Q K^T and
-//   dP = dO V^T put one key per lane column, so P^T and dS^T feed
-//   dv += P^T dO and dk += dS^T Q directly, with dO^T and Q^T read by
-//   transposing LDS reads.  The two parity waves of a key block add their
-//   partial sums through LDS in a fixed order.  No atomics anywhere: results
-//   are bitwise repeatable.
+// k_dkdv: one block per 256-key tile and kv head; wave w owns keys
+//   [r0 + 32 w, r0 + 32 w + 32) for every query row.  K of a wave's keys stays
+//   in registers, V of the tile in LDS; Q and dO tiles of 64 query rows (plus
+//   their LSE, D and segment starts) arrive by direct-to-LDS loads, double
+//   buffered.  S = Q K^T and dP = dO V^T put one key per lane column, so P^T
+//   and dS^T feed dv += P^T dO and dk += dS^T Q directly, with dO^T and Q^T
+//   read by transposing LDS reads.  No atomics anywhere: results are bitwise
+//   repeatable.
 #include "spd_attn_dev.h"
 
 namespace spd {
@@ -30,6 +29,7 @@ using namespace dev;
 constexpr int kWaves = 8;
 constexpr int kBN = 64;      // keys per tile in k_dq
 constexpr int kQB = 64;      // query rows per staged block in k_dkdv
+constexpr int kDkdvKeys = 256;  // keys per k_dkdv tile (8 waves x 32)
 
 // D[h, row] = sum_d dO[row, h, d] O[row, h, d];  L2[h, row] = lse[h, row] log2(e);
 // segp[row] = seg_start[row].  The three arrays have a row stride of Tp >= T + 64
@@ -94,7 +94,9 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
   constexpr int WPH = NW / HPW;
   constexpr int KS = D / 16;
   constexpr int TB = BN * D * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];   // [stage][K | V]
+  constexpr int STAGES = 3;
+  constexpr int PER = 2 * (BN * D / 8) / (NW * 64);
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * 2 * TB];   // [stage][K | V]
 
   const int tile_rank = blockIdx.x / HG;
   if (tile_rank >= *ntiles) return;
@@ -148,20 +150,20 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
   const int n = nA + nB;
   auto kt_of = [&](int i) { return i < nA ? t.u0 + i * BN : t.s0 + (i - nA) * BN; };
 
-  dma_rows<BN, D, NW>(smem, k, kt_of(0), T, Hkv, kvh, wave, lane);
-  dma_rows<BN, D, NW>(smem + TB, v, kt_of(0), T, Hkv, kvh, wave, lane);
+  auto issue = [&](int i) {
+    char *st = smem + (i % STAGES) * 2 * TB;
+    dma_rows<BN, D, NW>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
+    dma_rows<BN, D, NW>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
+  };
+  for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
 
   for (int i = 0; i < n; ++i) {
-    wait_tile();
-    if (i + 1 < n) {
-      char *nxt = smem + ((i + 1) & 1) * 2 * TB;
-      dma_rows<BN, D, NW>(nxt, k, kt_of(i + 1), T, Hkv, kvh, wave, lane);
-      dma_rows<BN, D, NW>(nxt + TB, v, kt_of(i + 1), T, Hkv, kvh, wave, lane);
-    }
+    wait_ring<STAGES, PER>(i, n);
+    if (i + STAGES - 1 < n) issue(i + STAGES - 1);
     const int kt = kt_of(i);
     const bool phaseA = i < nA;
     if (qlast < qw0 || (!phaseA && kt > qlast)) continue;
-    const char *Ks = smem + (i & 1) * 2 * TB;
+    const char *Ks = smem + (i % STAGES) * 2 * TB;
     const char *Vs = Ks + TB;
     const bool need_mask = phaseA ? (kt + BN > t.u1) : (kt + BN - 1 > qw0 || kt < seg_hi);
 #pragma unroll
@@ -211,20 +213,12 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
 
 // ---------------------------------------------------------------------------- dk / dv
 
-// Direct-to-LDS copy of the per-row scalars of query rows [r0, r0 + 64) of
-// head h: log2-LSE, D (float, row stride Tp) and seg_start (int).  One wave,
-// lanes 0..47 (16 lanes x 16 bytes per array); r0 < T and Tp >= T + 64 keep
-// every read inside the padded arrays.
-__device__ inline void dma_row_scalars(char *dst, const float *L2buf, const float *Dbuf, const int *segp, int r0,
-                                       int Tp, int h, int lane) {
-  if (lane < 48) {
-    const int arr = lane >> 4, part = lane & 15;
-    const int64_t at = int64_t(h) * Tp + r0 + 4 * part;
-    const void *g = arr == 0 ? static_cast<const void *>(L2buf + at)
-                             : arr == 1 ? static_cast<const void *>(Dbuf + at)
-                                        : static_cast<const void *>(segp + r0 + 4 * part);
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)(dst), 16, 0, 0);
-  }
+// Direct-to-LDS copy of one per-row scalar array for query rows [r0, r0 + 64):
+// 16 lanes x 16 bytes.  r0 < T and the arrays' row stride Tp >= T + 64 keep
+// the read inside them.
+__device__ inline void dma_scalars(char *dst, const void *src, int lane) {
+  if (lane < 16)
+    __builtin_amdgcn_global_load_lds(static_cast<const char *>(src) + lane * 16, (lds_void *)(dst), 16, 0, 0);
 }
 
 template <int D>
@@ -236,15 +230,14 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
                                                       const float *__restrict__ Dbuf,
                                                       const int *__restrict__ segp, int Tp, __bf16 *__restrict__ dk,
                                                       __bf16 *__restrict__ dv, float scale_log2, float scale) {
-  constexpr int NW = kWaves, QB = kQB;
+  constexpr int NW = kWaves, QB = kQB, BK = kDkdvKeys;   // 64 query rows per block, 256 keys per tile
   constexpr int KS = D / 16;
   constexpr int TB = QB * D * 2;                    // one Q or dO tile
-  constexpr int SB = 3 * QB * 4;                    // LSE2 | D | seg_start of the block
-  constexpr int STAGE = 2 * TB + 1024;              // Q | dO | scalars (padded)
-  constexpr int XB = 4 * 32 * D * 4;                // one exchange round: 4 key blocks x 32 keys x D floats
-  constexpr int SMEM = (2 * STAGE > XB) ? 2 * STAGE : XB;
-  static_assert(SB <= 1024, "row scalars fit their slot");
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  constexpr int STAGE = 2 * TB + 1024;              // Q | dO | LSE2, D, seg_start (256 B each)
+  constexpr int STAGES = 2;
+  constexpr int PER = 2 * (QB * D / 8) / (NW * 64); // direct-to-LDS tile loads per wave per block
+  constexpr int VT = BK * D * 2;                    // V rows of the tile's keys
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE + VT];
 
   const int tile_rank = blockIdx.x / Hkv;
   if (tile_rank >= *ntiles) return;
@@ -253,20 +246,19 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
   const int wave = wave_id();
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
-  const int kblk = wave & 3, par = wave >> 2;
-  const int key = t.r0 + 32 * kblk + col;   // this lane's key column
+  const int kmin = t.r0 + 32 * wave;        // this wave's keys: kmin .. kmin + 31
+  const int key = kmin + col;               // this lane's key column
   const bool kvalid = key < t.r1;
   const int ratio = Hq / Hkv;
+  char *Vt = smem + STAGES * STAGE;
 
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 kf[KS];
   {
     const int64_t off = (int64_t(kvalid ? key : t.r0) * Hkv + kvh) * D + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = kvalid ? ld_global8(k + off + 16 * ks) : zero8();
-      vf[ks] = kvalid ? ld_global8(v + off + 16 * ks) : zero8();
-    }
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = kvalid ? ld_global8(k + off + 16 * ks) : zero8();
   }
+  dma_rows<BK, D, NW>(Vt, v, t.r0, T, Hkv, kvh, wave, lane);
   f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
@@ -274,122 +266,122 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
     dva[i] = zero16();
   }
 
-  // This wave's 32 query rows of a staged block: rows 32 par .. 32 par + 31.
-  int roff[KS];   // row reads of Q / dO (A operands): row 32 par + col, chunk 2 ks + half
+  // A-operand row reads of Q / dO: row 32 m + col, chunk 2 ks + half (m = 32-row
+  // half of the block, an immediate offset).  The V rows of this wave's keys
+  // (row 32 wave + col) share the low row bits, so the same offsets apply.
+  int roff[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) roff[ks] = swz_off<D>(32 * par + col, 2 * ks + half);
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = swz_off<D>(col, 2 * ks + half);
+  const char *Vw = Vt + 32 * wave * D * 2;
+  // dO^T / Q^T reads (transposing): rows 32 m + 16 j + 8 w + 4 (grp / 2) + s16 / 4
   const int grp = lane >> 4, s16 = lane & 15;
-  int toff[D / 32][2];   // dO^T / Q^T reads: rows 32 par + 16 ks + 8 w + 4 (grp/2) + s16/4
+  int toff[D / 32][2];
 #pragma unroll
   for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-      const int row = 32 * par + 8 * w + 4 * (grp >> 1) + (s16 >> 2);
+      const int row = 8 * w + 4 * (grp >> 1) + (s16 >> 2);
       const int dcol = 32 * dblk + 16 * (grp & 1) + 4 * (s16 & 3);
       toff[dblk][w] = swz_off<D>(row, dcol >> 3) + ((dcol & 7) << 1);
     }
 
-  const int nA = (t.u1 - t.u0 + QB - 1) / QB;   // masked query rows
-  const int nB = (t.e0 - t.s0 + QB - 1) / QB;   // unmasked query rows
+  // Block order, per query head: the group's response rows (unmasked, the same
+  // blocks for every prompt key tile of the group), then the masked rows from
+  // the top down, so concurrently running tiles sweep the same rows together.
+  const int nA = (t.u1 - t.u0 + QB - 1) / QB;   // masked query rows [u0, u1)
+  const int nB = (t.e0 - t.s0 + QB - 1) / QB;   // unmasked query rows [s0, e0)
   const int nper = nA + nB;
   const int n = nper * ratio;
   auto blk_of = [&](int i, int &h, int &qb, bool &masked, int &qend) {
     const int hh = i / nper, j = i % nper;
     h = kvh * ratio + hh;
-    masked = j < nA;
-    qb = masked ? t.u0 + j * QB : t.s0 + (j - nA) * QB;
+    masked = j >= nB;
+    qb = masked ? t.u0 + (nper - 1 - j) * QB : t.s0 + j * QB;
     qend = masked ? t.u1 : t.e0;
   };
-  auto issue = [&](int i, char *st) {
+  auto issue = [&](int i) {
     int h, qb, qend;
     bool masked;
     blk_of(i, h, qb, masked, qend);
+    char *st = smem + (i % STAGES) * STAGE;
     dma_rows<QB, D, NW>(st, q, qb, T, Hq, h, wave, lane);
     dma_rows<QB, D, NW>(st + TB, dout, qb, T, Hq, h, wave, lane);
-    if (wave == 0) dma_row_scalars(st + 2 * TB, L2buf, Dbuf, segp, qb, Tp, h, lane);
+    if (wave == 0) dma_scalars(st + 2 * TB, L2buf + int64_t(h) * Tp + qb, lane);
+    if (wave == 1) dma_scalars(st + 2 * TB + 256, Dbuf + int64_t(h) * Tp + qb, lane);
+    if (wave == 2) dma_scalars(st + 2 * TB + 512, segp + qb, lane);
   };
 
-  if (n > 0) issue(0, smem);
+  for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
   for (int i = 0; i < n; ++i) {
-    wait_tile();
-    if (i + 1 < n) issue(i + 1, smem + ((i + 1) & 1) * STAGE);
+    // waves 0-2 issue one extra load per block: waiting for PER-sized stages
+    // only makes them wait longer, never too little
+    wait_ring<STAGES, PER>(i, n);
+    if (i + STAGES - 1 < n) issue(i + STAGES - 1);
     int h, qb, qend;
     bool masked;
     blk_of(i, h, qb, masked, qend);
-    const int row0 = qb + 32 * par;                 // first query row of this wave
-    const int kmin = t.r0 + 32 * kblk;              // smallest key of this wave
-    if (row0 >= qend) continue;                     // no rows
-    if (masked && row0 + 31 < kmin) continue;       // every row precedes every key
-    const char *Qs = smem + (i & 1) * STAGE;
+    if (masked && qb + QB - 1 < kmin) continue;     // every row of the block precedes every key
+    const char *Qs = smem + (i % STAGES) * STAGE;
     const char *Ds = Qs + TB;
-    const float *sL2 = reinterpret_cast<const float *>(Qs + 2 * TB);        // entry e = row qb + e
+    const float *sL2 = reinterpret_cast<const float *>(Qs + 2 * TB);         // entry e = row qb + e
     const float *sD = reinterpret_cast<const float *>(Qs + 2 * TB + 256);
     const int *sSeg = reinterpret_cast<const int *>(Qs + 2 * TB + 512);
-
-    f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma(ld_lds8(Qs + roff[ks]), kf[ks], s);
-      dp = mfma(ld_lds8(Ds + roff[ks]), vf[ks], dp);
-    }
-    bf16x8 pf[2], dsf[2];
-    const bool need_mask = masked || row0 + 31 >= qend;
+    for (int m = 0; m < QB / 32; ++m) {
+      const int row0 = qb + 32 * m;
+      if (row0 >= qend || (masked && row0 + 31 < kmin)) continue;
+      const char *Qm = Qs + 32 * m * D * 2;
+      const char *Dm = Ds + 32 * m * D * 2;
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int e = 32 * par + c_row(r, half);       // entry in the block's scalar arrays
-      const int row = qb + e;
-      float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -sL2[e]));
-      float ds = p * (dp[r] - sD[e]);
-      if (need_mask) {
-        bool vis = row < qend;
-        if (masked) vis = vis && key <= row && key >= sSeg[e];
-        p = vis ? p : 0.0f;
-        ds = vis ? ds : 0.0f;
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma(ld_lds8(Qm + roff[ks]), kf[ks], s);
+        dp = mfma(ld_lds8(Dm + roff[ks]), ld_lds8(Vw + roff[ks]), dp);
       }
-      pf[r >> 3][r & 7] = static_cast<__bf16>(p);
-      dsf[r >> 3][r & 7] = static_cast<__bf16>(ds);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int dblk = 0; dblk < D / 32; ++dblk) {
-        const bf16x8 bdo = ld_lds_tr_pair(Ds + toff[dblk][0] + j * 16 * D * 2, Ds + toff[dblk][1] + j * 16 * D * 2);
-        const bf16x8 bq = ld_lds_tr_pair(Qs + toff[dblk][0] + j * 16 * D * 2, Qs + toff[dblk][1] + j * 16 * D * 2);
-        dva[dblk] = mfma(pf[j], bdo, dva[dblk]);
-        dka[dblk] = mfma(dsf[j], bq, dka[dblk]);
-      }
-  }
-
-  // Combine the two parities of each key block through LDS, in a fixed order:
-  // round 1 parity 1 hands its dk partial to parity 0, which writes dk;
-  // round 2 parity 0 hands its dv partial to parity 1, which writes dv.
-  float *xch = reinterpret_cast<float *>(smem);
-  const int xbase = kblk * 32 * D;   // floats
-  auto put = [&](const f32x16 *a) {
-#pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xch[xbase + c_row(r, half) * D + 32 * dblk + col] = a[dblk][r];
-  };
-  auto take_and_store = [&](const f32x16 *a, __bf16 *out, float mul) {
-#pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk)
+      bf16x8 pf[2], dsf[2];
+      const bool need_mask = masked || row0 + 31 >= qend;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kr = c_row(r, half);
-        const float val = (a[dblk][r] + xch[xbase + kr * D + 32 * dblk + col]) * mul;
-        const int kk = t.r0 + 32 * kblk + kr;
-        if (kk < t.r1) out[(int64_t(kk) * Hkv + kvh) * D + 32 * dblk + col] = static_cast<__bf16>(val);
+        const int e = 32 * m + c_row(r, half);
+        const int row = qb + e;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -sL2[e]));
+        float ds = p * (dp[r] - sD[e]);
+        if (need_mask) {
+          bool vis = row < qend;
+          if (masked) vis = vis && key <= row && key >= sSeg[e];
+          p = vis ? p : 0.0f;
+          ds = vis ? ds : 0.0f;
+        }
+        pf[r >> 3][r & 7] = static_cast<__bf16>(p);
+        dsf[r >> 3][r & 7] = static_cast<__bf16>(ds);
       }
-  };
-  wait_tile();
-  if (par == 1) put(dka);
-  __syncthreads();
-  if (par == 0) take_and_store(dka, dk, scale);
-  __syncthreads();
-  if (par == 0) put(dva);
-  __syncthreads();
-  if (par == 1) take_and_store(dva, dv, 1.0f);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dblk = 0; dblk < D / 32; ++dblk) {
+          const int o0 = toff[dblk][0] + (32 * m + 16 * j) * D * 2;
+          const int o1 = toff[dblk][1] + (32 * m + 16 * j) * D * 2;
+          const bf16x8 bdo = ld_lds_tr_pair(Ds + o0, Ds + o1);
+          const bf16x8 bq = ld_lds_tr_pair(Qs + o0, Qs + o1);
+          dva[dblk] = mfma(pf[j], bdo, dva[dblk]);
+          dka[dblk] = mfma(dsf[j], bq, dka[dblk]);
+        }
+    }
+  }
+
+  // dv / dk: register r of dblk holds key row c_row(r, half) of the wave's 32
+  // keys and column 32 dblk + col.
+#pragma unroll
+  for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = kmin + c_row(r, half);
+      if (kk < t.r1) {
+        const int64_t off = (int64_t(kk) * Hkv + kvh) * D + 32 * dblk + col;
+        dk[off] = static_cast<__bf16>(dka[dblk][r] * scale);
+        dv[off] = static_cast<__bf16>(dva[dblk][r]);
+      }
+    }
 }
 
 int bwd_heads_per_block(const spd_attn_desc &d) {
@@ -400,7 +392,7 @@ int bwd_heads_per_block(const spd_attn_desc &d) {
 }  // namespace
 
 int dq_bf16_rows_per_tile(const spd_attn_desc &d) { return 32 * (kWaves / bwd_heads_per_block(d)); }
-int dkdv_bf16_rows_per_tile(const spd_attn_desc &) { return 128; }
+int dkdv_bf16_rows_per_tile(const spd_attn_desc &) { return kDkdvKeys; }
 
 spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *qtiles, const int *nq,
                          int64_t capq, const Tile *ktiles, const int *nk, int64_t capk, const void *q, const void *k,

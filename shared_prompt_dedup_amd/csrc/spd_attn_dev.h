@@ -8,9 +8,12 @@
 // the same ones.  A result reused as an operand (probabilities, dS) therefore
 // lists, in lane half h, the rows {4h..4h+3, 8+4h..8+4h+3} of each 16-row step.
 //
-// Tiles live in LDS row-major with 16-byte chunks XOR-swizzled by row (slot =
-// chunk ^ (row mod chunks-per-row)), which keeps a half-wave's 16-byte reads of
-// one column on distinct banks.  They are filled with direct-to-LDS loads
+// Tiles live in LDS row-major with 16-byte chunks XOR-swizzled by row: slot =
+// chunk ^ f(row), f a bit permutation of the row's low bits (b3 b2 b1 b0 ->
+// b3 b1 b0 b2).  Sixteen consecutive rows read at one chunk land on sixteen
+// distinct slots (conflict-free 16-byte row reads), and the four consecutive
+// rows a transposing read touches (32 bytes each) land on four distinct
+// 32-byte bank groups.  They are filled with direct-to-LDS loads
 // (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l), so no
 // registers or ALU time are spent staging them.
 //
@@ -67,11 +70,19 @@ __device__ inline bf16x8 ld_lds_tr_pair(const char *p0, const char *p1) {
 // Row (0..31) of register r of a 32x32 result for lane half h.
 __device__ inline int c_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Row swizzle: bits b3 b2 b1 b0 of the row become b3 b1 b0 b2 (limited to the
+// chunks per row).
+template <int D>
+__device__ inline int swz_of(int row) {
+  constexpr int CPR = D / 8;
+  const int r = row & (CPR - 1);
+  return ((r & 3) << 1) | ((r >> 2) & 1) | (r & ~7);
+}
+
 // Byte offset of 16-byte chunk `chunk` of row `row` in a swizzled tile of D columns.
 template <int D>
 __device__ inline int swz_off(int row, int chunk) {
-  constexpr int CPR = D / 8;
-  return row * (D * 2) + ((chunk ^ (row & (CPR - 1))) << 4);
+  return row * (D * 2) + ((chunk ^ swz_of<D>(row)) << 4);
 }
 
 // Direct-to-LDS copy of rows [r0, r0 + ROWS) of a [*, H, D] bf16 tensor (head
@@ -89,7 +100,7 @@ __device__ inline void dma_rows(char *tile, const __bf16 *src, int r0, int T, in
     const int L = blk * 64 + lane;
     const int r = L / CPR;
     const int slot = L % CPR;
-    const int chunk = slot ^ (r & (CPR - 1));
+    const int chunk = slot ^ swz_of<D>(r);
     const int row = min(r0 + r, T - 1);
     const char *g = reinterpret_cast<const char *>(src + (int64_t(row) * H + hh) * D) + (chunk << 4);
     __builtin_amdgcn_global_load_lds(g, (lds_void *)(tile + blk * 1024), 16, 0, 0);
@@ -100,6 +111,27 @@ __device__ inline void dma_rows(char *tile, const __bf16 *src, int r0, int T, in
 // included), then for every wave of the block.
 __device__ inline void wait_tile() {
   __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// s_waitcnt immediate that waits only until at most N vector-memory operations
+// of this wave are outstanding (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] in [15:14]).
+template <int N>
+struct VmCnt {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  static constexpr int imm = (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
+};
+
+// Ring wait for tile i of n when the ring keeps up to STAGES tiles in flight
+// and each tile costs PER direct-to-LDS loads per wave: tiles i+1 .. i+STAGES-2
+// may still be loading.  Then a block barrier.
+template <int STAGES, int PER>
+__device__ inline void wait_ring(int i, int n) {
+  if (i + STAGES - 2 < n)
+    __builtin_amdgcn_s_waitcnt(VmCnt<(STAGES - 2) * PER>::imm);
+  else
+    __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 }
 

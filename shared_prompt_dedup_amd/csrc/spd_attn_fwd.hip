@@ -39,7 +39,9 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
   constexpr int WPH = NW / HPW;          // waves per query head
   constexpr int KS = D / 16;             // contraction steps over head_dim
   constexpr int TB = BN * D * 2;         // bytes of one K or V tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];   // [stage][K | V]
+  constexpr int STAGES = 3;              // tiles in flight: the ring hides two tiles of load latency
+  constexpr int PER = 2 * (BN * D / 8) / (NW * 64);   // direct-to-LDS loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * 2 * TB];   // [stage][K | V]
 
   const int tile_rank = blockIdx.x / HG;
   if (tile_rank >= *ntiles) return;
@@ -93,20 +95,20 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
   const int n = nA + nB;
   auto kt_of = [&](int i) { return i < nA ? t.u0 + i * BN : t.s0 + (i - nA) * BN; };
 
-  dma_rows<BN, D, NW>(smem, k, kt_of(0), T, Hkv, kvh, wave, lane);
-  dma_rows<BN, D, NW>(smem + TB, v, kt_of(0), T, Hkv, kvh, wave, lane);
+  auto issue = [&](int i) {
+    char *st = smem + (i % STAGES) * 2 * TB;
+    dma_rows<BN, D, NW>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
+    dma_rows<BN, D, NW>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
+  };
+  for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
 
   for (int i = 0; i < n; ++i) {
-    wait_tile();
-    if (i + 1 < n) {
-      char *nxt = smem + ((i + 1) & 1) * 2 * TB;
-      dma_rows<BN, D, NW>(nxt, k, kt_of(i + 1), T, Hkv, kvh, wave, lane);
-      dma_rows<BN, D, NW>(nxt + TB, v, kt_of(i + 1), T, Hkv, kvh, wave, lane);
-    }
+    wait_ring<STAGES, PER>(i, n);
+    if (i + STAGES - 1 < n) issue(i + STAGES - 1);
     const int kt = kt_of(i);
     const bool phaseA = i < nA;
     if (qlast < qw0 || (!phaseA && kt > qlast)) continue;   // nothing this wave can see
-    const char *Ks = smem + (i & 1) * 2 * TB;
+    const char *Ks = smem + (i % STAGES) * 2 * TB;
     const char *Vs = Ks + TB;
     const bool need_mask = phaseA ? (kt + BN > t.u1) : (kt + BN - 1 > qw0 || kt < seg_hi);
 
