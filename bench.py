@@ -171,6 +171,18 @@ def main():
             ach = work / (ms * 1e-3) / 1e9
             kernels[kname] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    # Practical HBM reference: a plain device-to-device copy of 1 GiB (read + write).
+    src_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst_buf = torch.empty_like(src_buf)
+    dst_buf.copy_(src_buf)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        dst_buf.copy_(src_buf)
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src_buf, dst_buf
     dom = max(kernels, key=lambda kk: kernels[kk]["ms"])
     roof = dict(kernels[dom])
     roof.pop("ms")
@@ -197,6 +209,7 @@ def main():
         "attention_kernels_tflops": round((fwd_flops + bwd_flops) / (attn_ms * 1e-3) / 1e12, 2),
         "roofline": roof,
         "kernels": kernels,
+        "hbm_copy_gbs": round(copy_gbs, 1),
     }
     if args.cpu_baseline == "on":
         result["cpu_baseline"] = cpu_baseline(w, bt, pairs)

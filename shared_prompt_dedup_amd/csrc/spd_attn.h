@@ -36,9 +36,9 @@ inline int64_t tile_capacity(int64_t B, int64_t T, int rows_per_tile) {
 
 // Builds a tile list on the device (one block), sorted by decreasing cost so
 // that the heaviest tiles are dispatched first.  `tmp` and `out` hold
-// `cap` tiles; *n_out receives the count.
-spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, Tile *tmp,
-                              Tile *out, int *n_out, int64_t cap, hipStream_t st);
+// `cap` tiles, `goff` B + 1 ints of scratch; *n_out receives the count.
+spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, int *goff,
+                              Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st);
 
 // fp32 correctness kernels (plain arithmetic, one row per thread).
 spd_status attn_fwd_f32(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *tiles,

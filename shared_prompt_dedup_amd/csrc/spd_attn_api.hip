@@ -20,62 +20,81 @@ __device__ inline int segment_end(const spd_plan &plan, int x) {
   return plan.resp_off[b] + plan.resp_len[b];
 }
 
-__global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int T, int TM, int mode,
-                                                               int cap, Tile *__restrict__ tmp,
+// Group g's rows: prompt [po, ro), responses [ro, re), clipped to [0, Tdev).
+struct GroupRows {
+  int po, ro, re, np, nr;
+};
+
+__device__ inline GroupRows group_rows(const spd_plan &plan, int g, int G, int Tdev, int TM) {
+  GroupRows r;
+  r.po = min(plan.prompt_off[g], Tdev);
+  r.ro = min(r.po + plan.prompt_len[g], Tdev);
+  r.re = (g + 1 < G) ? min(plan.prompt_off[g + 1], Tdev) : Tdev;
+  r.re = max(r.re, r.ro);
+  r.np = (r.ro - r.po + TM - 1) / TM;
+  r.nr = (r.re - r.ro + TM - 1) / TM;
+  return r;
+}
+
+// One block: per-group tile counts and their exclusive scan (goff[0..G]),
+// then one thread per tile (its group found by binary search over goff),
+// then a counting sort by decreasing cost.
+__global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int T, int TM, int mode, int cap,
+                                                               int *__restrict__ goff, Tile *__restrict__ tmp,
                                                                Tile *__restrict__ out, int *__restrict__ n_out) {
   __shared__ int scan_tmp[kPlanThreads / 64];
   __shared__ int hist[kBuckets];
-  __shared__ int s_total;
   const int tid = threadIdx.x;
   const int G = plan.counts[0];
   const int Tdev = min(plan.counts[1], T);
-  // 1. tiles per group, exclusive scan over groups, emit (one thread per group)
   int base = 0;
   for (int g0 = 0; g0 < G; g0 += kPlanThreads) {
     const int g = g0 + tid;
-    int po = 0, ro = 0, re = 0, np = 0, nr = 0;
+    int cnt = 0;
     if (g < G) {
-      po = min(plan.prompt_off[g], Tdev);
-      ro = min(po + plan.prompt_len[g], Tdev);
-      re = (g + 1 < G) ? min(plan.prompt_off[g + 1], Tdev) : Tdev;
-      re = max(re, ro);
-      np = (ro - po + TM - 1) / TM;
-      nr = (re - ro + TM - 1) / TM;
+      const GroupRows r = group_rows(plan, g, G, Tdev, TM);
+      cnt = r.np + r.nr;
     }
     int total = 0;
-    const int ex = block_exclusive_scan(np + nr, scan_tmp, total);
-    if (g < G) {
-      int idx = base + ex;
-      for (int i = 0; i < np + nr && idx < cap; ++i, ++idx) {
-        Tile t;
-        const bool prompt = i < np;
-        const int lo = prompt ? po : ro;
-        const int hi = prompt ? ro : re;
-        const int j = prompt ? i : i - np;
-        t.r0 = lo + j * TM;
-        t.r1 = min(hi, t.r0 + TM);
-        t.kind = prompt ? 0 : 1;
-        if (mode == kQueryTiles) {
-          t.u0 = prompt ? 0 : po;
-          t.u1 = prompt ? 0 : ro;
-          t.s0 = plan.seg_start[t.r0];
-          t.e0 = 0;
-          t.cost = (t.u1 - t.u0) + (t.r1 - t.s0);
-        } else {
-          t.u0 = t.r0;
-          t.u1 = prompt ? ro : segment_end(plan, t.r1 - 1);
-          t.s0 = prompt ? ro : 0;
-          t.e0 = prompt ? re : 0;
-          t.cost = (t.u1 - t.u0) + (t.e0 - t.s0);
-        }
-        tmp[idx] = t;
-      }
-    }
+    const int ex = block_exclusive_scan(cnt, scan_tmp, total);
+    if (g < G) goff[g] = base + ex;
     base += total;
   }
+  if (tid == 0) goff[G] = base;
+  __syncthreads();
   const int N = min(base, cap);
-  // 2. counting sort by decreasing cost (order inside a bucket is free: it
-  //    only changes which block runs a tile first, never a result)
+  for (int i = tid; i < N; i += kPlanThreads) {
+    int lo = 0, hi = G - 1;   // last group whose first tile is <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (goff[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int g = lo;
+    const GroupRows r = group_rows(plan, g, G, Tdev, TM);
+    const int j = i - goff[g];
+    const bool prompt = j < r.np;
+    Tile t;
+    t.r0 = (prompt ? r.po : r.ro) + (prompt ? j : j - r.np) * TM;
+    t.r1 = min(prompt ? r.ro : r.re, t.r0 + TM);
+    t.kind = prompt ? 0 : 1;
+    if (mode == kQueryTiles) {
+      t.u0 = prompt ? 0 : r.po;
+      t.u1 = prompt ? 0 : r.ro;
+      t.s0 = plan.seg_start[t.r0];
+      t.e0 = 0;
+      t.cost = (t.u1 - t.u0) + (t.r1 - t.s0);
+    } else {
+      t.u0 = t.r0;
+      t.u1 = prompt ? r.ro : segment_end(plan, t.r1 - 1);
+      t.s0 = prompt ? r.ro : 0;
+      t.e0 = prompt ? r.re : 0;
+      t.cost = (t.u1 - t.u0) + (t.e0 - t.s0);
+    }
+    tmp[i] = t;
+  }
+  // counting sort by decreasing cost (order inside a bucket is free: it only
+  // changes which block runs a tile first, never a result)
   int shift = 0;
   while ((Tdev >> shift) >= kBuckets) ++shift;
   for (int i = tid; i < kBuckets; i += kPlanThreads) hist[i] = 0;
@@ -85,7 +104,6 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
     atomicAdd(&hist[bkt], 1);
   }
   __syncthreads();
-  // exclusive scan of the 4096 buckets, 4 per thread
   int c[4], s = 0;
   for (int e = 0; e < 4; ++e) {
     c[e] = hist[tid * 4 + e];
@@ -109,11 +127,11 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
 
 }  // namespace
 
-spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, Tile *tmp,
-                              Tile *out, int *n_out, int64_t cap, hipStream_t st) {
+spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, int *goff,
+                              Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st) {
   static_assert(kBuckets == 4 * kPlanThreads, "bucket scan assumes 4 buckets per thread");
   hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(kPlanThreads), 0, st, plan, int(T), rows_per_tile, int(mode),
-                     int(cap), tmp, out, n_out);
+                     int(cap), goff, tmp, out, n_out);
   return check_launch();
 }
 
@@ -121,7 +139,7 @@ namespace {
 
 struct AttnWs {
   Tile *qtiles = nullptr, *ktiles = nullptr, *tmp = nullptr;
-  int *counts = nullptr;
+  int *counts = nullptr, *goff = nullptr;
   float *Dbuf = nullptr, *L2buf = nullptr;
   int *segp = nullptr;
   int64_t capq = 0, capk = 0, Tp = 0;
@@ -161,6 +179,8 @@ AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
   off += tb;
   if (p) w.counts = reinterpret_cast<int *>(p + off);
   off += 256;
+  if (p) w.goff = reinterpret_cast<int *>(p + off);
+  off += round_up(size_t(B + 1) * 4, 256);
   w.bytes = off;
   return w;
 }
@@ -203,7 +223,7 @@ extern "C" spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_pl
   if (T == 0) return SPD_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnWs w = carve(*desc, plan->B, T, workspace);
-  SPD_TRY(launch_build_tiles(*plan, T, q_rows(*desc), kQueryTiles, w.tmp, w.qtiles, w.counts, w.capq, st));
+  SPD_TRY(launch_build_tiles(*plan, T, q_rows(*desc), kQueryTiles, w.goff, w.tmp, w.qtiles, w.counts, w.capq, st));
   if (desc->dtype == SPD_F32)
     return attn_fwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, static_cast<const float *>(q),
                         static_cast<const float *>(k), static_cast<const float *>(v), static_cast<float *>(o), lse,
@@ -223,8 +243,8 @@ extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_pl
   if (T == 0) return SPD_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnWs w = carve(*desc, plan->B, T, workspace);
-  SPD_TRY(launch_build_tiles(*plan, T, dq_rows(*desc), kQueryTiles, w.tmp, w.qtiles, w.counts, w.capq, st));
-  SPD_TRY(launch_build_tiles(*plan, T, k_rows(*desc), kKeyTiles, w.tmp, w.ktiles, w.counts + 1, w.capk, st));
+  SPD_TRY(launch_build_tiles(*plan, T, dq_rows(*desc), kQueryTiles, w.goff, w.tmp, w.qtiles, w.counts, w.capq, st));
+  SPD_TRY(launch_build_tiles(*plan, T, k_rows(*desc), kKeyTiles, w.goff, w.tmp, w.ktiles, w.counts + 1, w.capk, st));
   if (desc->dtype == SPD_F32)
     return attn_bwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, w.ktiles, w.counts + 1, w.capk,
                         static_cast<const float *>(q), static_cast<const float *>(k), static_cast<const float *>(v),
