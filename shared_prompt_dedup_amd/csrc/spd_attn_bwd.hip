@@ -7,7 +7,7 @@
 // A prompt key's dk / dv sum over the prompt's own causal queries and over
 // every response row of its group; query heads sharing a kv head add into it.
 //
-// k_bwd_pre: D and the log2-scaled LSE per (head, row).
+// k_bwd_pre: D and lse / scale per (head, row), and each row's segment end.
 // k_dq: one block per query tile (as the forward), K and V tiles by
 //   direct-to-LDS loads, S^T = K Q^T, dP^T = V dO^T, dq^T += K^T dS^T with
 //   K^T read by transposing LDS reads.
@@ -31,16 +31,18 @@ constexpr int kBN = 64;      // keys per tile in k_dq
 constexpr int kQB = 64;      // query rows per staged block in k_dkdv
 constexpr int kDkdvKeys = 256;  // keys per k_dkdv tile (8 waves x 32)
 
-// D[h, row] = sum_d dO[row, h, d] O[row, h, d];  L2[h, row] = lse[h, row] log2(e);
-// segp[row] = seg_start[row].  The three arrays have a row stride of Tp >= T + 64
-// so that 64-row blocks starting below T never leave them; the padding rows
-// are set to 0 and are masked by every reader.
+// Per (head, row): D = sum_d dO O and Ls = lse / scale, so that
+// P = exp2(c (s - Ls)) with c = scale log2(e) and s the raw score Q.K.  Per
+// row: send = one past the last row of the row's segment (prompt or response).
+// D and Ls have a row stride of Tp >= T + 64 so that 64-row blocks starting
+// below T never leave them; the padding rows are set to 0 and every reader
+// masks them.
 template <int D>
-__global__ void __launch_bounds__(256) k_bwd_pre(int64_t rows_x_heads, int Hq, int T, int Tp,
+__global__ void __launch_bounds__(256) k_bwd_pre(int64_t rows_x_heads, int Hq, int T, int Tp, float inv_scale,
                                                  const __bf16 *__restrict__ o, const __bf16 *__restrict__ dout,
-                                                 const float *__restrict__ lse, const int *__restrict__ seg_start,
-                                                 float *__restrict__ Dbuf, float *__restrict__ L2buf,
-                                                 int *__restrict__ segp) {
+                                                 const float *__restrict__ lse, spd_plan plan,
+                                                 float *__restrict__ Dbuf, float *__restrict__ Lbuf,
+                                                 int *__restrict__ send) {
   constexpr int LPR = D / 8;     // lanes per (row, head)
   constexpr int RPW = 64 / LPR;  // (row, head) pairs per wave
   const int lane = threadIdx.x & 63;
@@ -61,21 +63,29 @@ __global__ void __launch_bounds__(256) k_bwd_pre(int64_t rows_x_heads, int Hq, i
     const int h = static_cast<int>(i % Hq);
     const int64_t at = int64_t(h) * Tp + row;
     Dbuf[at] = s;
-    L2buf[at] = lse[int64_t(h) * T + row] * kLog2e;
-    if (h == 0) segp[row] = seg_start[row];
+    Lbuf[at] = lse[int64_t(h) * T + row] * inv_scale;
+    if (h == 0) {
+      const int src = plan.src[row];
+      const int b = static_cast<int>(src / plan.S);
+      const int64_t t = src - int64_t(b) * plan.S;
+      int end;
+      if (t < plan.P) {
+        const int g = plan.group_of[b];
+        end = plan.prompt_off[g] + plan.prompt_len[g];
+      } else {
+        end = plan.resp_off[b] + plan.resp_len[b];
+      }
+      send[row] = end;
+    }
   }
-  // zero the padding rows [T, Tp) of every array
-  const int64_t pad = int64_t(Tp - T) * (Hq + 1);
+  // zero the padding rows [T, Tp) of D and Ls
+  const int64_t pad = int64_t(Tp - T) * Hq;
   const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t nthreads = int64_t(gridDim.x) * blockDim.x;
   for (int64_t j = tid; j < pad; j += nthreads) {
     const int64_t a = j / (Tp - T), r = T + j % (Tp - T);
-    if (a < Hq) {
-      Dbuf[a * Tp + r] = 0.0f;
-      L2buf[a * Tp + r] = 0.0f;
-    } else {
-      segp[r] = 0;
-    }
+    Dbuf[a * Tp + r] = 0.0f;
+    Lbuf[a * Tp + r] = 0.0f;
   }
 }
 
@@ -85,7 +95,7 @@ template <int D, int HPW>
 __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ tiles, const int *__restrict__ ntiles,
                                                     int HG, int Hq, int Hkv, int T, const __bf16 *__restrict__ q,
                                                     const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
-                                                    const float *__restrict__ L2buf,
+                                                    const float *__restrict__ Lbuf,
                                                     const __bf16 *__restrict__ dout, const float *__restrict__ Dbuf,
                                                     int Tp, __bf16 *__restrict__ dq,
                                                     const int *__restrict__ seg_start, float scale_log2,
@@ -115,8 +125,9 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
   const bool qvalid = qrow < t.r1;
   const int seg_q = qvalid ? seg_start[qrow] : 0x7fffffff;
   const int seg_hi = qlast >= qw0 ? seg_start[qlast] : 0x7fffffff;
-  const float lse2 = qvalid ? L2buf[int64_t(h) * Tp + qrow] : 0.0f;
-  const float Dq = qvalid ? Dbuf[int64_t(h) * Tp + qrow] : 0.0f;
+  // accumulators start at -lse/scale and -D: then P = exp2(c s) and dS = P dP
+  const float s_init = qvalid ? -Lbuf[int64_t(h) * Tp + qrow] : 0.0f;
+  const float dp_init = qvalid ? -Dbuf[int64_t(h) * Tp + qrow] : 0.0f;
 
   bf16x8 qf[KS], df[KS];
   {
@@ -168,7 +179,12 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
     const bool need_mask = phaseA ? (kt + BN > t.u1) : (kt + BN - 1 > qw0 || kt < seg_hi);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = s_init;
+        dp[r] = dp_init;
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma(ld_lds8(Ks + roff[ks] + kb * 32 * D * 2), qf[ks], s);
@@ -177,13 +193,13 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
       bf16x8 dsf[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -lse2));
+        float p = __builtin_amdgcn_exp2f(s[r] * scale_log2);
         if (need_mask) {
           const int key = kt + 32 * kb + c_row(r, half);
           const bool vis = phaseA ? (key < t.u1) : (key <= qrow && key >= seg_q);
           p = vis ? p : 0.0f;
         }
-        dsf[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] - Dq));
+        dsf[r >> 3][r & 7] = static_cast<__bf16>(p * dp[r]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -213,7 +229,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
 
 // ---------------------------------------------------------------------------- dk / dv
 
-// Direct-to-LDS copy of one per-row scalar array for query rows [r0, r0 + 64):
+// Direct-to-LDS copy of one per-row float array for query rows [r0, r0 + 64):
 // 16 lanes x 16 bytes.  r0 < T and the arrays' row stride Tp >= T + 64 keep
 // the read inside them.
 __device__ inline void dma_scalars(char *dst, const void *src, int lane) {
@@ -225,15 +241,15 @@ template <int D>
 __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ tiles, const int *__restrict__ ntiles,
                                                       int Hq, int Hkv, int T, const __bf16 *__restrict__ q,
                                                       const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
-                                                      const float *__restrict__ L2buf,
+                                                      const float *__restrict__ Lbuf,
                                                       const __bf16 *__restrict__ dout,
                                                       const float *__restrict__ Dbuf,
-                                                      const int *__restrict__ segp, int Tp, __bf16 *__restrict__ dk,
+                                                      const int *__restrict__ send, int Tp, __bf16 *__restrict__ dk,
                                                       __bf16 *__restrict__ dv, float scale_log2, float scale) {
   constexpr int NW = kWaves, QB = kQB, BK = kDkdvKeys;   // 64 query rows per block, 256 keys per tile
   constexpr int KS = D / 16;
   constexpr int TB = QB * D * 2;                    // one Q or dO tile
-  constexpr int STAGE = 2 * TB + 1024;              // Q | dO | LSE2, D, seg_start (256 B each)
+  constexpr int STAGE = 2 * TB + 512;               // Q | dO | lse/scale, D (256 B each)
   constexpr int STAGES = 2;
   constexpr int PER = 2 * (QB * D / 8) / (NW * 64); // direct-to-LDS tile loads per wave per block
   constexpr int VT = BK * D * 2;                    // V rows of the tile's keys
@@ -251,6 +267,10 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
   const bool kvalid = key < t.r1;
   const int ratio = Hq / Hkv;
   char *Vt = smem + STAGES * STAGE;
+  // A masked query row sees this key iff key <= row < end of the key's segment
+  // (a prompt key's masked rows are its own prompt's; a response key's are its
+  // own response's).
+  const int kend = kvalid ? send[key] : 0;
 
   bf16x8 kf[KS];
   {
@@ -306,14 +326,13 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
     char *st = smem + (i % STAGES) * STAGE;
     dma_rows<QB, D, NW>(st, q, qb, T, Hq, h, wave, lane);
     dma_rows<QB, D, NW>(st + TB, dout, qb, T, Hq, h, wave, lane);
-    if (wave == 0) dma_scalars(st + 2 * TB, L2buf + int64_t(h) * Tp + qb, lane);
+    if (wave == 0) dma_scalars(st + 2 * TB, Lbuf + int64_t(h) * Tp + qb, lane);
     if (wave == 1) dma_scalars(st + 2 * TB + 256, Dbuf + int64_t(h) * Tp + qb, lane);
-    if (wave == 2) dma_scalars(st + 2 * TB + 512, segp + qb, lane);
   };
 
   for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
   for (int i = 0; i < n; ++i) {
-    // waves 0-2 issue one extra load per block: waiting for PER-sized stages
+    // waves 0-1 issue one extra load per block: waiting for PER-sized stages
     // only makes them wait longer, never too little
     wait_ring<STAGES, PER>(i, n);
     if (i + STAGES - 1 < n) issue(i + STAGES - 1);
@@ -323,16 +342,28 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
     if (masked && qb + QB - 1 < kmin) continue;     // every row of the block precedes every key
     const char *Qs = smem + (i % STAGES) * STAGE;
     const char *Ds = Qs + TB;
-    const float *sL2 = reinterpret_cast<const float *>(Qs + 2 * TB);         // entry e = row qb + e
-    const float *sD = reinterpret_cast<const float *>(Qs + 2 * TB + 256);
-    const int *sSeg = reinterpret_cast<const int *>(Qs + 2 * TB + 512);
+    const char *sL = Qs + 2 * TB;        // float entry e = row qb + e: lse / scale
+    const char *sD = Qs + 2 * TB + 256;  // D
 #pragma unroll
     for (int m = 0; m < QB / 32; ++m) {
       const int row0 = qb + 32 * m;
       if (row0 >= qend || (masked && row0 + 31 < kmin)) continue;
       const char *Qm = Qs + 32 * m * D * 2;
       const char *Dm = Ds + 32 * m * D * 2;
-      f32x16 s = zero16(), dp = zero16();
+      // accumulators start at -lse/scale and -D of their rows: register r holds
+      // row 32 m + 8 (r / 4) + 4 half + r % 4, four consecutive rows per group
+      f32x16 s, dp;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e = 32 * m + 8 * g + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sL + 4 * e);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sD + 4 * e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[4 * g + j] = -l4[j];
+          dp[4 * g + j] = -d4[j];
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma(ld_lds8(Qm + roff[ks]), kf[ks], s);
@@ -342,13 +373,12 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
       const bool need_mask = masked || row0 + 31 >= qend;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int e = 32 * m + c_row(r, half);
-        const int row = qb + e;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -sL2[e]));
-        float ds = p * (dp[r] - sD[e]);
+        const int row = row0 + c_row(r, half);
+        float p = __builtin_amdgcn_exp2f(s[r] * scale_log2);
+        float ds = p * dp[r];
         if (need_mask) {
           bool vis = row < qend;
-          if (masked) vis = vis && key <= row && key >= sSeg[e];
+          if (masked) vis = vis && key <= row && row < kend;
           p = vis ? p : 0.0f;
           ds = vis ? ds : 0.0f;
         }
@@ -397,7 +427,7 @@ int dkdv_bf16_rows_per_tile(const spd_attn_desc &) { return kDkdvKeys; }
 spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *qtiles, const int *nq,
                          int64_t capq, const Tile *ktiles, const int *nk, int64_t capk, const void *q, const void *k,
                          const void *v, const void *o, const float *lse, const void *dout, void *dq, void *dk,
-                         void *dv, float *Dbuf, float *L2buf, int *segp, int64_t Tp, hipStream_t st) {
+                         void *dv, float *Dbuf, float *Lbuf, int *send, int64_t Tp, hipStream_t st) {
   const auto *qq = static_cast<const __bf16 *>(q);
   const auto *kk = static_cast<const __bf16 *>(k);
   const auto *vv = static_cast<const __bf16 *>(v);
@@ -409,11 +439,11 @@ spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
   const dim3 gpre(static_cast<unsigned>((waves + 3) / 4));
   prof_start(SPD_K_BWD_PRE, st);
   if (d.head_dim == 128)
-    hipLaunchKernelGGL(k_bwd_pre<128>, gpre, dim3(256), 0, st, n, d.num_q_heads, int(T), int(Tp), oo, dd, lse,
-                       plan.seg_start, Dbuf, L2buf, segp);
+    hipLaunchKernelGGL(k_bwd_pre<128>, gpre, dim3(256), 0, st, n, d.num_q_heads, int(T), int(Tp),
+                       1.0f / d.softmax_scale, oo, dd, lse, plan, Dbuf, Lbuf, send);
   else
-    hipLaunchKernelGGL(k_bwd_pre<64>, gpre, dim3(256), 0, st, n, d.num_q_heads, int(T), int(Tp), oo, dd, lse,
-                       plan.seg_start, Dbuf, L2buf, segp);
+    hipLaunchKernelGGL(k_bwd_pre<64>, gpre, dim3(256), 0, st, n, d.num_q_heads, int(T), int(Tp),
+                       1.0f / d.softmax_scale, oo, dd, lse, plan, Dbuf, Lbuf, send);
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_BWD_PRE, st);
 
@@ -429,7 +459,7 @@ spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
   prof_start(SPD_K_BWD_DQ, st);
 #define SPD_DQ_LAUNCH(DD, HH)                                                                                     \
   hipLaunchKernelGGL((k_dq<DD, HH>), gq, block, 0, st, qtiles, nq, HG, d.num_q_heads, d.num_kv_heads, int(T), qq, \
-                     kk, vv, L2buf, dd, Dbuf, int(Tp), dqq, plan.seg_start, sl2, d.softmax_scale)
+                     kk, vv, Lbuf, dd, Dbuf, int(Tp), dqq, plan.seg_start, sl2, d.softmax_scale)
   if (d.head_dim == 128) {
     if (hpw == 4) SPD_DQ_LAUNCH(128, 4);
     else if (hpw == 2) SPD_DQ_LAUNCH(128, 2);
@@ -445,10 +475,10 @@ spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
   prof_start(SPD_K_BWD_DKDV, st);
   if (d.head_dim == 128)
     hipLaunchKernelGGL(k_dkdv<128>, gk, block, 0, st, ktiles, nk, d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv,
-                       L2buf, dd, Dbuf, segp, int(Tp), dkk, dvv, sl2, d.softmax_scale);
+                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, sl2, d.softmax_scale);
   else
     hipLaunchKernelGGL(k_dkdv<64>, gk, block, 0, st, ktiles, nk, d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv,
-                       L2buf, dd, Dbuf, segp, int(Tp), dkk, dvv, sl2, d.softmax_scale);
+                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, sl2, d.softmax_scale);
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_BWD_DKDV, st);
   return SPD_OK;
