@@ -31,8 +31,9 @@ constexpr int kBN = 64;      // keys per tile in k_dq
 constexpr int kQB = 64;      // query rows per staged block in k_dkdv
 constexpr int kDkdvKeys = 256;  // keys per k_dkdv tile (8 waves x 32)
 
-// Per (head, row): D = sum_d dO O and Ls = lse / scale, so that
-// P = exp2(c (s - Ls)) with c = scale log2(e) and s the raw score Q.K.  Per
+// Per (head, row): nD = -sum_d dO O and nL = -lse / scale, so that
+// P = exp2(c (s + nL)) with c = scale log2(e) and s the raw score Q.K, and
+// dS = P (dP + nD); score and dP accumulators can start at nL and nD.  Per
 // row: send = one past the last row of the row's segment (prompt or response).
 // D and Ls have a row stride of Tp >= T + 64 so that 64-row blocks starting
 // below T never leave them; the padding rows are set to 0 and every reader
@@ -62,8 +63,8 @@ __global__ void __launch_bounds__(256) k_bwd_pre(int64_t rows_x_heads, int Hq, i
     const int64_t row = i / Hq;
     const int h = static_cast<int>(i % Hq);
     const int64_t at = int64_t(h) * Tp + row;
-    Dbuf[at] = s;
-    Lbuf[at] = lse[int64_t(h) * T + row] * inv_scale;
+    Dbuf[at] = -s;
+    Lbuf[at] = -lse[int64_t(h) * T + row] * inv_scale;
     if (h == 0) {
       const int src = plan.src[row];
       const int b = static_cast<int>(src / plan.S);
@@ -125,9 +126,10 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
   const bool qvalid = qrow < t.r1;
   const int seg_q = qvalid ? seg_start[qrow] : 0x7fffffff;
   const int seg_hi = qlast >= qw0 ? seg_start[qlast] : 0x7fffffff;
-  // accumulators start at -lse/scale and -D: then P = exp2(c s) and dS = P dP
-  const float s_init = qvalid ? -Lbuf[int64_t(h) * Tp + qrow] : 0.0f;
-  const float dp_init = qvalid ? -Dbuf[int64_t(h) * Tp + qrow] : 0.0f;
+  // P = exp2(c s + s_bias), dS = P (dP + dp_bias) with s_bias = -c lse/scale
+  // = -lse log2(e) and dp_bias = -D (the arrays hold -lse/scale and -D)
+  const float s_bias = qvalid ? Lbuf[int64_t(h) * Tp + qrow] * scale_log2 : 0.0f;
+  const float dp_bias = qvalid ? Dbuf[int64_t(h) * Tp + qrow] : 0.0f;
 
   bf16x8 qf[KS], df[KS];
   {
@@ -179,34 +181,34 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
     const bool need_mask = phaseA ? (kt + BN > t.u1) : (kt + BN - 1 > qw0 || kt < seg_hi);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = s_init;
-        dp[r] = dp_init;
-      }
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma(ld_lds8(Ks + roff[ks] + kb * 32 * D * 2), qf[ks], s);
         dp = mfma(ld_lds8(Vs + roff[ks] + kb * 32 * D * 2), df[ks], dp);
       }
+      if (need_mask) {
+        keep_branch();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + 32 * kb + c_row(r, half);
+          const bool vis = phaseA ? (key < t.u1) : (key <= qrow && key >= seg_q);
+          s[r] = vis ? s[r] : -INFINITY;
+        }
+      }
       bf16x8 dsf[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(s[r] * scale_log2);
-        if (need_mask) {
-          const int key = kt + 32 * kb + c_row(r, half);
-          const bool vis = phaseA ? (key < t.u1) : (key <= qrow && key >= seg_q);
-          p = vis ? p : 0.0f;
-        }
-        dsf[r >> 3][r & 7] = static_cast<__bf16>(p * dp[r]);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, s_bias));
+        dsf[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] + dp_bias));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int ks = 2 * kb + j;
 #pragma unroll
         for (int dblk = 0; dblk < D / 32; ++dblk) {
-          const bf16x8 a = ld_lds_tr_pair(Ks + toff[dblk][0] + ks * 16 * D * 2, Ks + toff[dblk][1] + ks * 16 * D * 2);
+          const bf16x8 a =
+              ld_lds_tr_pair(Ks + toff[dblk][0] + ks * 16 * D * 2, Ks + toff[dblk][1] + ks * 16 * D * 2);
           acc[dblk] = mfma(a, dsf[j], acc[dblk]);
         }
       }
@@ -271,6 +273,10 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
   // (a prompt key's masked rows are its own prompt's; a response key's are its
   // own response's).
   const int kend = kvalid ? send[key] : 0;
+  // Segment ends never decrease with the key, so lane 0's (the wave's first
+  // key) is the smallest; kmax is the wave's last valid key.
+  const int kend0 = __builtin_amdgcn_readfirstlane(kend);
+  const int kmax = min(kmin + 31, t.r1 - 1);
 
   bf16x8 kf[KS];
   {
@@ -360,8 +366,8 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
         const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sD + 4 * e);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          s[4 * g + j] = -l4[j];
-          dp[4 * g + j] = -d4[j];
+          s[4 * g + j] = l4[j];
+          dp[4 * g + j] = d4[j];
         }
       }
 #pragma unroll
@@ -369,21 +375,26 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
         s = mfma(ld_lds8(Qm + roff[ks]), kf[ks], s);
         dp = mfma(ld_lds8(Dm + roff[ks]), ld_lds8(Vw + roff[ks]), dp);
       }
-      bf16x8 pf[2], dsf[2];
-      const bool need_mask = masked || row0 + 31 >= qend;
+      // every (row, key) of the 32 x 32 block visible: rows inside the range,
+      // and for masked rows all past the wave's last key and before the
+      // earliest segment end among its keys
+      const bool full = row0 + 31 < qend && (!masked || (row0 >= kmax && row0 + 31 < kend0));
+      if (!full) {
+        keep_branch();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + c_row(r, half);
-        float p = __builtin_amdgcn_exp2f(s[r] * scale_log2);
-        float ds = p * dp[r];
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + c_row(r, half);
           bool vis = row < qend;
           if (masked) vis = vis && key <= row && row < kend;
-          p = vis ? p : 0.0f;
-          ds = vis ? ds : 0.0f;
+          s[r] = vis ? s[r] : -INFINITY;
         }
+      }
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[r] * scale_log2);
         pf[r >> 3][r & 7] = static_cast<__bf16>(p);
-        dsf[r >> 3][r & 7] = static_cast<__bf16>(ds);
+        dsf[r >> 3][r & 7] = static_cast<__bf16>(p * dp[r]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j)

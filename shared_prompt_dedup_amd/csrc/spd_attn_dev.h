@@ -136,6 +136,11 @@ __device__ inline void wait_ring(int i, int n) {
   __syncthreads();
 }
 
+// Marks a wave-uniform branch as worth keeping: the compiler may not
+// speculate a volatile asm, so the guarded work (e.g. masking) runs only when
+// the condition holds instead of being turned into selects on every pass.
+__device__ inline void keep_branch() { asm volatile(""); }
+
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 }  // namespace dev

@@ -120,13 +120,14 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
       for (int ks = 0; ks < KS; ++ks) s[kb] = mfma(ld_lds8(Ks + koff[ks] + kb * 32 * D * 2), qf[ks], s[kb]);
     }
     if (need_mask) {
+      keep_branch();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt + 32 * kb + c_row(r, half);
           const bool vis = phaseA ? (key < t.u1) : (key <= qrow && key >= seg_q);
-          if (!vis) s[kb][r] = -INFINITY;
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
     }
     float mt = -INFINITY;
@@ -156,7 +157,8 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dblk = 0; dblk < D / 32; ++dblk) {
-        const bf16x8 a = ld_lds_tr_pair(Vs + voff[dblk][0] + ks * 16 * D * 2, Vs + voff[dblk][1] + ks * 16 * D * 2);
+        const bf16x8 a =
+            ld_lds_tr_pair(Vs + voff[dblk][0] + ks * 16 * D * 2, Vs + voff[dblk][1] + ks * 16 * D * 2);
         oacc[dblk] = mfma(a, pf[ks], oacc[dblk]);
       }
   }
