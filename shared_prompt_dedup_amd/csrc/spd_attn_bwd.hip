@@ -168,6 +168,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
     dma_rows<BN, D, NW>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
     dma_rows<BN, D, NW>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
   };
+  wait_vm_all();
   for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
 
   for (int i = 0; i < n; ++i) {
@@ -234,9 +235,8 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
 // Direct-to-LDS copy of one per-row float array for query rows [r0, r0 + 64):
 // 16 lanes x 16 bytes.  r0 < T and the arrays' row stride Tp >= T + 64 keep
 // the read inside them.
-__device__ inline void dma_scalars(char *dst, const void *src, int lane) {
-  if (lane < 16)
-    __builtin_amdgcn_global_load_lds(static_cast<const char *>(src) + lane * 16, (lds_void *)(dst), 16, 0, 0);
+__device__ inline void dma_scalars(char *dst, const float *src, int lane) {
+  if (lane < 16) dma16(src, static_cast<unsigned>(lane) * 16, dst);
 }
 
 template <int D>
@@ -284,6 +284,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = kvalid ? ld_global8(k + off + 16 * ks) : zero8();
   }
+  wait_vm_all();
   dma_rows<BK, D, NW>(Vt, v, t.r0, T, Hkv, kvh, wave, lane);
   f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll

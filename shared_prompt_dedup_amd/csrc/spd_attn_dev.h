@@ -9,13 +9,13 @@
 // lists, in lane half h, the rows {4h..4h+3, 8+4h..8+4h+3} of each 16-row step.
 //
 // Tiles live in LDS row-major with 16-byte chunks XOR-swizzled by row: slot =
-// chunk ^ f(row), f a bit permutation of the row's low bits (b3 b2 b1 b0 ->
-// b3 b1 b0 b2).  Sixteen consecutive rows read at one chunk land on sixteen
-// distinct slots (conflict-free 16-byte row reads), and the four consecutive
-// rows a transposing read touches (32 bytes each) land on four distinct
-// 32-byte bank groups.  They are filled with direct-to-LDS loads
-// (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l), so no
-// registers or ALU time are spent staging them.
+// chunk ^ f(row).  LDS serves 256 bytes (all 64 banks) per cycle: 16 lanes of a
+// 16-byte read, or 32 lanes of an 8-byte read.  f makes both patterns in use
+// conflict-free: sixteen consecutive rows read at one chunk land on sixteen
+// distinct slots, and a half-wave of transposing reads (4 consecutive rows x
+// 4 consecutive chunks, see below) lands on sixteen distinct slots.  The tiles
+// are filled with direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16
+// bytes land at M0 + 16 l), so no registers or ALU time are spent staging them.
 //
 // The transposed operands (V^T, K^T, Q^T, dO^T) are read straight from those
 // row-major tiles with ds_read_b64_tr_b16: in each 16-lane group, output lane
@@ -24,6 +24,8 @@
 // output lane i holds column c0 + i of rows key(0..3): the column-major slice
 // an MFMA operand needs, with the 4 rows free to choose.
 #pragma once
+
+#include <cstdint>
 
 #include "spd_attn.h"
 
@@ -71,19 +73,37 @@ __device__ inline bf16x8 ld_lds_tr_pair(const char *p0, const char *p1) {
 // Row (0..31) of register r of a 32x32 result for lane half h.
 __device__ inline int c_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Row swizzle: bits b3 b2 b1 b0 of the row become b3 b1 b0 b2 (limited to the
-// chunks per row).
+// Row swizzle.  256-byte rows (D = 128): f(r) = 4 (r % 4) + (r / 4) % 4, a
+// permutation of the 16 slots over 16 rows, whose four rows of an aligned
+// quad differ in the top two slot bits.  128-byte rows (D = 64, two rows per
+// bank cycle): f(r) = 4 ((r / 2) % 2) + (r / 4) % 4, a permutation of the 8
+// slots over the 8 rows of either parity, whose same-parity rows of a quad
+// differ in slot bit 2.
 template <int D>
 __device__ inline int swz_of(int row) {
-  constexpr int CPR = D / 8;
-  const int r = row & (CPR - 1);
-  return ((r & 3) << 1) | ((r >> 2) & 1) | (r & ~7);
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in a swizzled tile of D columns.
 template <int D>
 __device__ inline int swz_off(int row, int chunk) {
   return row * (D * 2) + ((chunk ^ swz_of<D>(row)) << 4);
+}
+
+// One direct-to-LDS load: lane l's 16 bytes at base + voff land at LDS
+// address lds + 16 l (lds wave-uniform, base a wave-uniform 64-bit address
+// held in SGPRs, voff a per-lane 32-bit byte offset).  It is issued from
+// inline assembly: the compiler, seeing an LDS DMA, would otherwise make every
+// later transposing LDS read wait for all outstanding vector loads, including
+// the prefetches of later stages.  Callers wait for completion themselves
+// (wait_ring, wait_tile) before a barrier publishes the data.  The s_nop is the
+// wait state an LDS DMA needs after M0 is written.
+__device__ inline void dma16(const void *base, unsigned voff, const char *lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)(lds))));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m) : "memory");
 }
 
 // Direct-to-LDS copy of rows [r0, r0 + ROWS) of a [*, H, D] bf16 tensor (head
@@ -95,6 +115,10 @@ __device__ inline void dma_rows(char *tile, const __bf16 *src, int r0, int T, in
   constexpr int CHUNKS = ROWS * CPR;
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
   constexpr int PER_WAVE = CHUNKS / (NW * 64);
+  const int rb = min(r0, T - 1);       // base row; rows rb + r, r <= rmax, stay below T
+  const int rmax = T - 1 - rb;
+  const __bf16 *base = src + (int64_t(rb) * H + hh) * D;
+  const unsigned row_bytes = static_cast<unsigned>(H) * D * 2;
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int blk = wave * PER_WAVE + i;
@@ -102,9 +126,8 @@ __device__ inline void dma_rows(char *tile, const __bf16 *src, int r0, int T, in
     const int r = L / CPR;
     const int slot = L % CPR;
     const int chunk = slot ^ swz_of<D>(r);
-    const int row = min(r0 + r, T - 1);
-    const char *g = reinterpret_cast<const char *>(src + (int64_t(row) * H + hh) * D) + (chunk << 4);
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)(tile + blk * 1024), 16, 0, 0);
+    const unsigned voff = static_cast<unsigned>(min(r, rmax)) * row_bytes + (chunk << 4);
+    dma16(base, voff, tile + blk * 1024);
   }
 }
 
@@ -123,6 +146,13 @@ struct VmCnt {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   static constexpr int imm = (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
 };
+
+// Waits for every outstanding vector-memory load of this wave.  Called after a
+// kernel's own register loads and before its first direct-to-LDS load: the
+// compiler cannot count the assembly-issued loads, so a register load it still
+// believed pending would make it wait for every load in flight, prefetches
+// included, at each use.
+__device__ inline void wait_vm_all() { __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm); }
 
 // Ring wait for tile i of n when the ring keeps up to STAGES tiles in flight
 // and each tile costs PER direct-to-LDS loads per wave: tiles i+1 .. i+STAGES-2

@@ -100,6 +100,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
     dma_rows<BN, D, NW>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
     dma_rows<BN, D, NW>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
   };
+  wait_vm_all();
   for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
 
   for (int i = 0; i < n; ++i) {
