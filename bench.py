@@ -16,6 +16,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -26,9 +27,44 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+from workloads import BENCH_WORKLOAD  # noqa: E402  (numpy only)
+
 METRIC = "split-attn fwd+bwd TFLOP/s & % bf16 MFMA peak; pack/reconstruct GB/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+# HBM traffic per launch from two rocprofv3 --pmc passes (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch) over `bench.py --steps 1 --warmup 1
+# --cpu-baseline off --profile-steps 1` on the default workload.  The same
+# counters read for the 1 GiB device-to-device copy in that run give the
+# scale factors (FETCH_SIZE counts half of what is read on this chip,
+# WRITE_SIZE counts exactly).  Valid only for the kernel sources hashed in
+# TRAFFIC_SOURCES: after any change there the figure is reported as null.
+TRAFFIC_FETCH_SCALE = 2.0
+TRAFFIC_WRITE_SCALE = 1.0
+TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
+                   "spd_internal.h", "spd_dedup.hip")
+TRAFFIC_SOURCES_SHA256 = "5e74486c25e0448f8f2659cebe17098a27f6a64afbc4aac62b91f218fc7eec30"
+TRAFFIC_KIB = {   # kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
+    "fwd": (221750, 99842), "bwd_pre": (104874, 25352), "bwd_dq": (272441, 98561), "bwd_dkdv": (623620, 98621),
+    "reconstruct": (49555, 557466), "pack_rows": (49551, 98336),
+}
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "shared_prompt_dedup_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """Calibrated HBM bytes per launch, or None when not measured for these sources."""
+    if workload != BENCH_WORKLOAD or kernel not in TRAFFIC_KIB or TRAFFIC_SOURCES_SHA256 != sources_sha256():
+        return None
+    fetch, write = TRAFFIC_KIB[kernel]
+    return round((fetch * TRAFFIC_FETCH_SCALE + write * TRAFFIC_WRITE_SCALE) * 1024)
 
 
 def attended_pairs(info):
@@ -43,10 +79,9 @@ def attended_pairs(info):
     return pairs
 
 
-def cpu_baseline(w, bt, pairs_per_head, budget_heads=1):
-    """The oracle, as it stands, on one query head of the same workload (fwd + bwd, fp64)."""
-    import numpy as np
-
+def cpu_baseline(w, bt, pairs_per_head, min_seconds=10.0):
+    """The oracle, as it stands, forward + backward (fp64) on query heads of the same
+    workload, one head at a time until at least `min_seconds` of CPU work."""
     import oracle
     from workloads import make_attn_inputs
     try:
@@ -59,16 +94,19 @@ def cpu_baseline(w, bt, pairs_per_head, budget_heads=1):
     _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
                                                   attention_mask=bt.attention_mask, use_unpad=w.use_unpad)
     x = make_attn_inputs(w, info["T"])
-    heads = list(range(budget_heads))
-    t0 = time.perf_counter()
-    oracle.split_attention_forward(x.q, x.k, x.v, info, heads=heads)
-    oracle.split_attention_backward(x.q, x.k, x.v, x.do, info, heads=heads)
-    dt = time.perf_counter() - t0
-    flops = 14 * w.head_dim * len(heads) * pairs_per_head
+    heads = 0
+    dt = 0.0
+    while heads < w.num_q_heads and dt < min_seconds:
+        t0 = time.perf_counter()
+        oracle.split_attention_forward(x.q, x.k, x.v, info, heads=[heads])
+        oracle.split_attention_backward(x.q, x.k, x.v, x.do, info, heads=[heads])
+        dt += time.perf_counter() - t0
+        heads += 1
+    flops = 14 * w.head_dim * heads * pairs_per_head
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
             "kind": "oracle",
             "sample": f"fp64 numpy oracle (non-deduplicated per-sample attention), forward+backward of "
-                      f"{len(heads)} of {w.num_q_heads} query heads over the full batch; {dt:.1f} s; "
+                      f"{heads} of {w.num_q_heads} query heads over the full batch; {dt:.1f} s; "
                       f"useful FLOPs counted as on the GPU; host cores available "
                       f"{len(os.sched_getaffinity(0))}, {platform.processor() or platform.machine()}"}
 
@@ -93,7 +131,7 @@ def main():
     import torch
 
     import shared_prompt_dedup_amd as spd
-    from workloads import BENCH_WORKLOAD, WORKLOADS, make_attn_inputs, make_batch
+    from workloads import WORKLOADS, make_attn_inputs, make_batch
 
     name = args.workload or BENCH_WORKLOAD
     w = WORKLOADS[name]
@@ -186,7 +224,7 @@ def main():
     dom = max(kernels, key=lambda kk: kernels[kk]["ms"])
     roof = dict(kernels[dom])
     roof.pop("ms")
-    roof = {"kernel": dom, **roof, "traffic": None}
+    roof = {"kernel": dom, **roof, "traffic": measured_traffic(dom, name)}
 
     attn_ms = sum(kern_ms[kk] for kk in ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv") if kern_ms.get(kk))
     result = {
