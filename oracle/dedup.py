@@ -161,6 +161,44 @@ def pack_rows(rows, info):
     return flat[info["src"]]
 
 
+def reconstruct_backward(dout, info):
+    """How Prompt Deduplication Works -- Correctness & Gradients: the gradient
+    flows back through the reconstruction.
+
+    ``reconstruct_sequences`` copies packed row ``j`` to every output position
+    that reads it, so the gradient of row ``j`` is the sum of the output
+    gradients at those positions: a prompt row collects its column from every
+    member of the group, a response row its own position; positions that read
+    nothing (dropped pads) contribute nothing.  Summed in fp64, samples in
+    ascending order.  ``dout [B, S, ...] -> [T, ...]`` (float64).
+    """
+    x = np.asarray(dout, dtype=np.float64)
+    out = np.zeros((info["T"],) + x.shape[2:], dtype=np.float64)
+    for b in range(info["B"]):
+        g = info["group_of"][b]
+        po, pl = info["prompt_off"][g], info["prompt_len"][g]
+        out[po:po + pl] += x[b, info["prompt_cols"][b]]
+        ro, rl = info["resp_off"][b], info["resp_len"][b]
+        out[ro:ro + rl] += x[b, info["resp_cols"][b]]
+    return out
+
+
+def pack_rows_backward(dpacked, info):
+    """Correctness & Gradients -- the gradient flows back through the
+    deduplication.
+
+    Packed row ``j`` was copied from exactly one position, ``src[j]``, so its
+    gradient goes back there; every other position (the prompt columns of the
+    members whose copy was not kept, dropped pads) receives 0.
+    ``dpacked [T, ...] -> [B, S, ...]`` in the input's dtype.
+    """
+    x = np.asarray(dpacked)
+    B, S = info["B"], info["S"]
+    out = np.zeros((B * S,) + x.shape[1:], dtype=x.dtype)
+    out[info["src"]] = x
+    return out.reshape((B, S) + x.shape[1:])
+
+
 def sample_rows(info, b):
     """Packed rows of sample ``b``'s own sequence: its group's prompt, then its response.
 

@@ -205,3 +205,113 @@ def test_reconstruct_round_trip():
     assert not Y[~keep].any()
     # 2-D input is accepted too and gives the same
     np.testing.assert_array_equal(oracle.reconstruct_sequences(packed, info), Y)
+
+
+# ---------------------------------------------------------------- backward of reconstruct / pack_rows
+# Correctness & Gradients: gradients flow back through the reconstruction and
+# the deduplication.  Both maps are linear, so their gradients are pinned by
+# the adjoint identity <F(x), y> = <x, F^T(y)>, by torch autograd through an
+# independent formulation (a gather by dst), and by closed forms.
+
+def _info(use_unpad, permute=True, resp_len_range=(0, 32)):
+    w = WORKLOADS["tiny_fp32"].scaled(resp_len_range=resp_len_range)
+    bt = make_batch(w, permute=permute)
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length,
+                                                  groups, uniq, attention_mask=bt.attention_mask,
+                                                  use_unpad=use_unpad)
+    return w, bt, groups, info
+
+
+def _adjoint_gap(fwd, bwd, x, y):
+    lhs = float(np.sum(fwd(x) * y))
+    rhs = float(np.sum(x * bwd(y)))
+    return abs(lhs - rhs), float(np.sum(np.abs(fwd(x) * y)))
+
+
+@pytest.mark.parametrize("use_unpad", [False, True])
+def test_reconstruct_backward_is_the_adjoint(use_unpad):
+    w, bt, groups, info = _info(use_unpad)
+    rng = np.random.default_rng(21)
+    for _ in range(4):
+        x = rng.standard_normal((info["T"], 3))
+        y = rng.standard_normal((w.batch, w.seq_len, 3))
+        gap, scale = _adjoint_gap(lambda a: oracle.reconstruct_sequences(a, info),
+                                  lambda a: oracle.reconstruct_backward(a, info), x, y)
+        assert gap <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("use_unpad", [False, True])
+def test_pack_rows_backward_is_the_adjoint(use_unpad):
+    w, bt, groups, info = _info(use_unpad)
+    rng = np.random.default_rng(22)
+    for _ in range(4):
+        x = rng.standard_normal((w.batch, w.seq_len, 3))
+        y = rng.standard_normal((info["T"], 3))
+        gap, scale = _adjoint_gap(lambda a: oracle.pack_rows(a, info),
+                                  lambda a: oracle.pack_rows_backward(a, info), x, y)
+        assert gap <= 1e-12 * scale
+
+
+def test_reconstruct_backward_matches_autograd_gather():
+    """torch autograd through reconstruct written as a gather by dst (zero row for dst = -1)."""
+    torch = pytest.importorskip("torch")
+    w, bt, groups, info = _info(True)
+    rng = np.random.default_rng(23)
+    x = torch.tensor(rng.standard_normal((info["T"], 4)), dtype=torch.float64, requires_grad=True)
+    y = torch.tensor(rng.standard_normal((w.batch * w.seq_len, 4)), dtype=torch.float64)
+    dst = torch.tensor(np.asarray(info["dst"]), dtype=torch.int64)
+    padded = torch.cat([x, torch.zeros((1, 4), dtype=torch.float64)])
+    out = padded[torch.where(dst >= 0, dst, torch.full_like(dst, info["T"]))]
+    (out * y).sum().backward()
+    ref = oracle.reconstruct_backward(y.numpy().reshape(w.batch, w.seq_len, 4), info)
+    np.testing.assert_allclose(x.grad.numpy(), ref, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("use_unpad", [False, True])
+def test_reconstruct_backward_ones_count_readers(use_unpad):
+    """All-ones output gradient: a prompt row collects one per member, a response row one."""
+    w, bt, groups, info = _info(use_unpad)
+    g = oracle.reconstruct_backward(np.ones((w.batch, w.seq_len)), info)
+    for gi, members in enumerate(groups):
+        po, pl = info["prompt_off"][gi], info["prompt_len"][gi]
+        assert (g[po:po + pl] == len(members)).all()
+        for b in members:
+            ro, rl = info["resp_off"][b], info["resp_len"][b]
+            assert (g[ro:ro + rl] == 1).all()
+    # every packed row is a prompt row or a response row
+    assert g.sum() == sum(len(m) * info["prompt_len"][i] for i, m in enumerate(groups)) + info["resp_len"].sum()
+
+
+@pytest.mark.parametrize("use_unpad", [False, True])
+def test_pack_rows_backward_marks_sources(use_unpad):
+    """All-ones packed gradient lands exactly on the first member's prompt and every response."""
+    w, bt, groups, info = _info(use_unpad)
+    d = oracle.pack_rows_backward(np.ones(info["T"], dtype=np.int64), info)
+    P = w.prompt_len
+    keep = bt.attention_mask != 0 if use_unpad else np.ones((w.batch, w.seq_len), bool)
+    expect = np.zeros((w.batch, w.seq_len), np.int64)
+    for members in groups:
+        expect[members[0], :P] = keep[members[0], :P]
+        for b in members:
+            expect[b, P:] = keep[b, P:]
+    np.testing.assert_array_equal(d, expect)
+    assert d.sum() == info["T"]
+
+
+def test_planted_mistake_in_reconstruct_backward_is_caught():
+    """A backward that forgets the non-first members fails the adjoint identity."""
+    w, bt, groups, info = _info(False, resp_len_range=None)
+
+    def wrong(dout, info):
+        out = oracle.reconstruct_backward(dout, info)
+        for gi, members in enumerate(groups):
+            po, pl = info["prompt_off"][gi], info["prompt_len"][gi]
+            out[po:po + pl] = np.asarray(dout)[members[0], info["prompt_cols"][members[0]]]
+        return out
+
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((info["T"], 3))
+    y = rng.standard_normal((w.batch, w.seq_len, 3))
+    gap, scale = _adjoint_gap(lambda a: oracle.reconstruct_sequences(a, info), lambda a: wrong(a, info), x, y)
+    assert gap > 1e-3 * scale
