@@ -2,11 +2,15 @@
 """Throughput of prompt-deduplicated split attention on one MI355X.
 
 One step is one pass of the whole hot path over one synthetic batch already
-resident in HBM:
+resident in HBM, forward and backward:
   group (spd_group) -> pack ids/positions (spd_pack) -> pack the per-token
   rows entering the layer (spd_pack_rows) -> split-attention forward
-  (spd_split_attn_fwd) -> backward (spd_split_attn_bwd) -> reconstruct the
-  attention output to [batch, seq, Hq*d] (spd_reconstruct).
+  (spd_split_attn_fwd) -> reconstruct the attention output to
+  [batch, seq, Hq*d] (spd_reconstruct);
+  then the gradient of that output back to the packed rows
+  (spd_reconstruct_bwd, which gives the attention's dO) -> split-attention
+  backward (spd_split_attn_bwd) -> the packed rows' gradient (dQ standing in
+  for it) back to [batch, seq, Hq*d] (spd_pack_rows_bwd).
 
 `value` is the useful split-attention forward+backward work per step
 (4*d*Hq FLOP per attended (query, key) pair forward, 10*d*Hq backward,
@@ -153,19 +157,22 @@ def main():
     pairs = attended_pairs(info)
     x = make_attn_inputs(w, T)
     conv = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    q, k, v, dout = conv(x.q_bits), conv(x.k_bits), conv(x.v_bits), conv(x.do_bits)
+    q, k, v = conv(x.q_bits), conv(x.k_bits), conv(x.v_bits)
     del x
     gen = torch.Generator(device=dev).manual_seed(w.seed)
     hidden = torch.randn((B, S, W), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    dout_full = torch.randn((B, S, W), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
     def step():
         g, u = spd.group(ids, R, return_lists=False)
         _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=w.use_unpad)
         packed = spd.pack_rows(hidden, inf)
         o, lse = spd.split_attn_fwd(q, k, v, inf)
-        dq, dk, dv = spd.split_attn_bwd(q, k, v, o, lse, dout, inf)
         out = spd.reconstruct(o.view(T, W), inf)
-        return packed, out, dq, dk, dv
+        dout = spd.reconstruct_bwd(dout_full, inf).view(T, Hq, d)
+        dq, dk, dv = spd.split_attn_bwd(q, k, v, o, lse, dout, inf)
+        dhidden = spd.pack_rows_bwd(dq.view(T, W), inf)
+        return packed, out, dhidden, dk, dv
 
     for _ in range(args.warmup):
         step()
@@ -195,6 +202,8 @@ def main():
         "bwd_pre": ("hbm", 2 * T * W * 2 + T * Hq * 4),
         "reconstruct": ("hbm", T * row_bytes + B * S * row_bytes),
         "pack_rows": ("hbm", 2 * T * row_bytes),
+        "reconstruct_bwd": ("hbm", B * S * row_bytes + T * row_bytes),
+        "pack_rows_bwd": ("hbm", T * row_bytes + B * S * row_bytes),
     }
     kernels = {}
     for kname, (bound, work) in kernel_work.items():

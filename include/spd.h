@@ -12,6 +12,9 @@
  *                           the deduplicated computation)
  *   spd_reconstruct      -- Core Algorithm, "Reconstructing Original Batch";
  *                           Phase 3, "Transparent Reconstruction"
+ *   spd_reconstruct_bwd, spd_pack_rows_bwd
+ *                        -- "Correctness & Gradients": gradients flow back
+ *                           through the reconstruction and the deduplication
  *
  * Conventions shared by every call
  * --------------------------------
@@ -158,6 +161,35 @@ spd_status spd_pack_rows(const spd_plan *plan, int64_t T, const void *rows, int6
 spd_status spd_reconstruct(const spd_plan *plan, int64_t T, const void *packed, int64_t row_bytes,
                            void *out, void *stream);
 
+/*
+ * Backward of spd_reconstruct ("Correctness & Gradients": the gradient flows
+ * back through the reconstruction).  reconstruct is linear, so its adjoint:
+ *   dpacked[j, :] = sum over every (b, t) with dst[b * S + t] == j of dout[b, t, :].
+ * A packed prompt row thus receives the sum over all members of its group
+ * (column t of each), added in ascending member order in fp32 and rounded
+ * once (round-to-nearest-even for bf16); a response row receives its own
+ * (b, t)'s gradient.  Rows of dout that map nowhere (unpad pads) are ignored.
+ *   dout       device [B, S, row_bytes], elements of type dtype.
+ *   dtype      SPD_F32 or SPD_BF16 (else SPD_ERR_UNSUPPORTED).
+ *   dpacked    device [T, row_bytes], same dtype; every row is written.
+ * row_bytes must be a positive multiple of 16.
+ */
+spd_status spd_reconstruct_bwd(const spd_plan *plan, int64_t T, const void *dout, int64_t row_bytes,
+                               int32_t dtype, void *dpacked, void *stream);
+
+/*
+ * Backward of spd_pack_rows (the adjoint of packed[j] = rows[src[j]]):
+ *   drows[src[j], :] = dpacked[j, :] for every packed row j, and zeros in every
+ * other (b, t) -- the prompt columns of group members other than the one the
+ * prompt was taken from, and rows that map nowhere (unpad pads).  Bytes are
+ * copied, so any element type works.
+ *   dpacked    device [T, row_bytes].
+ *   drows      device [B, S, row_bytes]; every row is written.
+ * row_bytes must be a positive multiple of 16.
+ */
+spd_status spd_pack_rows_bwd(const spd_plan *plan, int64_t T, const void *dpacked, int64_t row_bytes,
+                             void *drows, void *stream);
+
 /* ---------------------------------------------------------- split attention */
 
 typedef struct spd_attn_desc {
@@ -222,7 +254,9 @@ enum {
   SPD_K_BWD_DKDV = 3,     /* backward: dk / dv kernel */
   SPD_K_RECONSTRUCT = 4,  /* reconstruct gather (and the zero fill) */
   SPD_K_PACK_ROWS = 5,    /* row packing gather */
-  SPD_K_COUNT = 6
+  SPD_K_RECONSTRUCT_BWD = 6,  /* backward of reconstruct: segment sum */
+  SPD_K_PACK_ROWS_BWD = 7,    /* backward of pack_rows: scatter (and the zero fill) */
+  SPD_K_COUNT = 8
 };
 spd_status spd_profile_begin(void);
 spd_status spd_profile_end(int64_t *launches, double *total_ms);

@@ -9,9 +9,10 @@ fallback.  (The package itself imports without it so that the build step,
 """
 import importlib
 
-_API = ("Plan", "PromptGroups", "ReconstructionInfo", "SplitAttention", "create_deduplicated_batch",
-        "find_prompt_groups", "group", "pack", "pack_rows", "reconstruct", "reconstruct_sequences",
-        "split_attention", "split_attn_bwd", "split_attn_fwd", "profile_begin", "profile_end")
+_API = ("Plan", "PromptGroups", "ReconstructionInfo", "SplitAttention", "PackRows", "Reconstruct",
+        "create_deduplicated_batch", "find_prompt_groups", "group", "pack", "pack_rows", "pack_rows_bwd",
+        "reconstruct", "reconstruct_bwd", "reconstruct_sequences", "split_attention", "split_attn_bwd",
+        "split_attn_fwd", "profile_begin", "profile_end")
 _LIB = ("EXPORTED", "LIB_PATH", "SpdError")
 
 __all__ = list(_API + _LIB)

@@ -11,7 +11,8 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspd.so")
 
 SPD_OK = 0
-SPD_K_NAMES = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "reconstruct", "pack_rows")
+SPD_K_NAMES = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "reconstruct", "pack_rows", "reconstruct_bwd",
+               "pack_rows_bwd")
 SPD_F32 = 0
 SPD_BF16 = 1
 
@@ -46,6 +47,9 @@ _SIG = {
                                 ctypes.c_size_t, _P]),
     "spd_pack_rows": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, _P, ctypes.c_int64, _P, _P]),
     "spd_reconstruct": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, _P, ctypes.c_int64, _P, _P]),
+    "spd_reconstruct_bwd": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, _P, ctypes.c_int64,
+                                           ctypes.c_int32, _P, _P]),
+    "spd_pack_rows_bwd": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, _P, ctypes.c_int64, _P, _P]),
     "spd_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SpdAttnDesc), ctypes.c_int64, ctypes.c_int64]),
     "spd_split_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SpdAttnDesc), ctypes.POINTER(SpdPlan), ctypes.c_int64,
                                           _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),

@@ -165,8 +165,7 @@ def pack(input_ids: torch.Tensor, position_ids: torch.Tensor, response_length: i
     return dids[:T].view(1, T), dpos[:T].view(1, T), ReconstructionInfo(plan)
 
 
-def pack_rows(rows: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
-    """spd_pack_rows: ``rows [B, S, ...] -> [T, ...]`` with the plan's packing."""
+def _pack_rows(rows: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
     plan = info.plan
     _need_cuda(rows, "rows")
     if tuple(rows.shape[:2]) != (plan.B, plan.S):
@@ -179,12 +178,41 @@ def pack_rows(rows: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
     return out
 
 
-def reconstruct(dedup_hidden: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
-    """spd_reconstruct: ``[1, T, ...]`` or ``[T, ...]`` -> ``[B, S, ...]``."""
+def pack_rows_bwd(dpacked: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
+    """spd_pack_rows_bwd: ``[T, ...] -> [B, S, ...]``, each packed row's gradient back at its source cell,
+    zeros elsewhere."""
     plan = info.plan
-    x = dedup_hidden
-    if x.dim() >= 3 and x.shape[0] == 1 and x.shape[1] == plan.T:
-        x = x[0]
+    _need_cuda(dpacked, "dpacked")
+    if dpacked.shape[0] != plan.T:
+        raise ValueError(f"dpacked has {dpacked.shape[0]} rows, the plan has T = {plan.T}")
+    tail = tuple(dpacked.shape[1:])
+    row_bytes = (dpacked[0].numel() if dpacked.dim() > 1 else 1) * dpacked.element_size()
+    out = torch.empty((plan.B, plan.S) + tail, dtype=dpacked.dtype, device=dpacked.device)
+    check("spd_pack_rows_bwd", lib.spd_pack_rows_bwd(ctypes.byref(plan.c), plan.T, _ptr(dpacked), row_bytes,
+                                                     _ptr(out), _stream(dpacked.device)))
+    return out
+
+
+class PackRows(torch.autograd.Function):
+    """pack_rows with its backward (``spd_pack_rows_bwd``)."""
+
+    @staticmethod
+    def forward(ctx, rows, info):
+        ctx.info = info
+        return _pack_rows(rows, info)
+
+    @staticmethod
+    def backward(ctx, g):
+        return pack_rows_bwd(g.contiguous(), ctx.info), None
+
+
+def pack_rows(rows: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
+    """spd_pack_rows: ``rows [B, S, ...] -> [T, ...]`` with the plan's packing (differentiable)."""
+    return PackRows.apply(rows, info)
+
+
+def _reconstruct(x: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
+    plan = info.plan
     _need_cuda(x, "dedup_hidden")
     if x.shape[0] != plan.T:
         raise ValueError(f"dedup_hidden has {x.shape[0]} rows, the plan has T = {plan.T}")
@@ -194,6 +222,49 @@ def reconstruct(dedup_hidden: torch.Tensor, info: ReconstructionInfo) -> torch.T
     check("spd_reconstruct", lib.spd_reconstruct(ctypes.byref(plan.c), plan.T, _ptr(x), row_bytes, _ptr(out),
                                                  _stream(x.device)))
     return out
+
+
+def reconstruct_bwd(dout: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
+    """spd_reconstruct_bwd: ``dout [B, S, ...] -> [T, ...]``; a packed prompt row receives the sum of its
+    group members' gradients (fp32 accumulation, one rounding).  bf16 or fp32."""
+    plan = info.plan
+    _need_cuda(dout, "dout")
+    if tuple(dout.shape[:2]) != (plan.B, plan.S):
+        raise ValueError("dout must be [batch, seq_len, ...]")
+    if dout.dtype == torch.bfloat16:
+        dt = SPD_BF16
+    elif dout.dtype == torch.float32:
+        dt = SPD_F32
+    else:
+        raise TypeError("reconstruct_bwd supports bfloat16 and float32 gradients")
+    tail = tuple(dout.shape[2:])
+    row_bytes = dout[0, 0].numel() * dout.element_size()
+    out = torch.empty((plan.T,) + tail, dtype=dout.dtype, device=dout.device)
+    check("spd_reconstruct_bwd", lib.spd_reconstruct_bwd(ctypes.byref(plan.c), plan.T, _ptr(dout), row_bytes, dt,
+                                                         _ptr(out), _stream(dout.device)))
+    return out
+
+
+class Reconstruct(torch.autograd.Function):
+    """reconstruct with its backward (``spd_reconstruct_bwd``)."""
+
+    @staticmethod
+    def forward(ctx, x, info):
+        ctx.info = info
+        return _reconstruct(x, info)
+
+    @staticmethod
+    def backward(ctx, g):
+        return reconstruct_bwd(g.contiguous(), ctx.info), None
+
+
+def reconstruct(dedup_hidden: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
+    """spd_reconstruct: ``[1, T, ...]`` or ``[T, ...]`` -> ``[B, S, ...]`` (differentiable)."""
+    plan = info.plan
+    x = dedup_hidden
+    if x.dim() >= 3 and x.shape[0] == 1 and x.shape[1] == plan.T:
+        x = x[0]
+    return Reconstruct.apply(x, info)
 
 
 # ---------------------------------------------------------------------------- attention

@@ -380,7 +380,10 @@ __global__ void __launch_bounds__(kRowThreads) k_pack_rows(int64_t T, int64_t ve
 
 // Packed row j goes to every (b, t) that maps to it: for a prompt row, the
 // same column t of every member of the group (read once, written n times);
-// for a response row, its own (b, t).
+// for a response row, its own (b, t).  With SOURCE_ONLY (the backward of
+// pack_rows) only the row's source cell src[j] receives it and the other
+// members' copies of a prompt row receive zeros.
+template <bool SOURCE_ONLY>
 __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t S, int64_t P,
                                                               int64_t vec_per_row, spd_plan plan,
                                                               const u32x4 *__restrict__ packed,
@@ -410,11 +413,71 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
       for (int m = m0; m < m1; ++m) {
         const int64_t b = members ? members[m] : b0;
         u32x4 *o = out + (b * S + t) * vec_per_row;
+        const bool zero = SOURCE_ONLY && b != b0;
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
           const int64_t c = c0 + u * 64 + lane;
-          if (c < vec_per_row) stream_store(o + c, v[u]);
+          if (c < vec_per_row) stream_store(o + c, zero ? u32x4{0u, 0u, 0u, 0u} : v[u]);
         }
+      }
+    }
+  }
+}
+
+// Backward of reconstruct: packed row j receives the sum of the gradients of
+// every (b, t) that reads it -- for a prompt row, column t of each member of
+// the group, summed in ascending member order in fp32 and rounded once; for a
+// response row, its own (b, t).  E is the element type (bf16 or fp32).
+template <typename E>
+__global__ void __launch_bounds__(kRowThreads) k_reconstruct_bwd(int64_t T, int64_t S, int64_t P,
+                                                                  int64_t vec_per_row, spd_plan plan,
+                                                                  const u32x4 *__restrict__ dout,
+                                                                  u32x4 *__restrict__ dpacked) {
+  constexpr int EPV = 16 / sizeof(E);   // elements per 16-byte vector
+  const int lane = __lane_id();
+  const int64_t nwaves = int64_t(gridDim.x) * (kRowThreads / 64);
+  for (int64_t j = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; j < T; j += nwaves) {
+    const int64_t s = plan.src[j];
+    const int64_t b0 = s / S;
+    const int64_t t = s - b0 * S;
+    int m0 = 0, m1 = 1;
+    const int32_t *members = nullptr;
+    if (t < P) {
+      const int g = plan.group_of[b0];
+      m0 = plan.grp_off[g];
+      m1 = plan.grp_off[g + 1];
+      members = plan.grp_idx;
+    }
+    u32x4 *o = dpacked + j * vec_per_row;
+    for (int64_t c0 = 0; c0 < vec_per_row; c0 += 64 * kU) {
+      float acc[kU][EPV];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
+      for (int m = m0; m < m1; ++m) {
+        const int64_t b = members ? members[m] : b0;
+        const u32x4 *in = dout + (b * S + t) * vec_per_row;
+        u32x4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int64_t c = c0 + u * 64 + lane;
+          v[u] = c < vec_per_row ? in[c] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const auto x = __builtin_bit_cast(E __attribute__((ext_vector_type(EPV))), v[u]);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[u][e] += static_cast<float>(x[e]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        E __attribute__((ext_vector_type(EPV))) y;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) y[e] = static_cast<E>(acc[u][e]);
+        if (c < vec_per_row) stream_store(o + c, __builtin_bit_cast(u32x4, y));
       }
     }
   }
@@ -549,7 +612,7 @@ extern "C" spd_status spd_reconstruct(const spd_plan *plan, int64_t T, const voi
   const int64_t vpr = row_bytes / 16;
   prof_start(SPD_K_RECONSTRUCT, st);
   if (T > 0) {
-    hipLaunchKernelGGL(k_reconstruct, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, plan->S, plan->P, vpr,
+    hipLaunchKernelGGL(k_reconstruct<false>, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, plan->S, plan->P, vpr,
                        *plan, static_cast<const u32x4 *>(packed), static_cast<u32x4 *>(out));
     SPD_LAUNCH_CHECK();
   }
@@ -558,6 +621,48 @@ extern "C" spd_status spd_reconstruct(const spd_plan *plan, int64_t T, const voi
                      plan->counts, static_cast<u32x4 *>(out));
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_RECONSTRUCT, st);
+  return SPD_OK;
+}
+
+extern "C" spd_status spd_reconstruct_bwd(const spd_plan *plan, int64_t T, const void *dout, int64_t row_bytes,
+                                          int32_t dtype, void *dpacked, void *stream) {
+  SPD_TRY(validate_plan(plan));
+  if (!dout || !dpacked || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if (dtype != SPD_F32 && dtype != SPD_BF16) return SPD_ERR_UNSUPPORTED;
+  if (row_bytes % 16 || !aligned16(dout) || !aligned16(dpacked)) return SPD_ERR_ALIGNMENT;
+  if (T == 0) return SPD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t vpr = row_bytes / 16;
+  prof_start(SPD_K_RECONSTRUCT_BWD, st);
+  if (dtype == SPD_BF16)
+    hipLaunchKernelGGL(k_reconstruct_bwd<__bf16>, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, plan->S, plan->P,
+                       vpr, *plan, static_cast<const u32x4 *>(dout), static_cast<u32x4 *>(dpacked));
+  else
+    hipLaunchKernelGGL(k_reconstruct_bwd<float>, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, plan->S, plan->P,
+                       vpr, *plan, static_cast<const u32x4 *>(dout), static_cast<u32x4 *>(dpacked));
+  SPD_LAUNCH_CHECK();
+  prof_stop(SPD_K_RECONSTRUCT_BWD, st);
+  return SPD_OK;
+}
+
+extern "C" spd_status spd_pack_rows_bwd(const spd_plan *plan, int64_t T, const void *dpacked, int64_t row_bytes,
+                                        void *drows, void *stream) {
+  SPD_TRY(validate_plan(plan));
+  if (!dpacked || !drows || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if (row_bytes % 16 || !aligned16(dpacked) || !aligned16(drows)) return SPD_ERR_ALIGNMENT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t vpr = row_bytes / 16;
+  prof_start(SPD_K_PACK_ROWS_BWD, st);
+  if (T > 0) {
+    hipLaunchKernelGGL(k_reconstruct<true>, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, plan->S, plan->P, vpr,
+                       *plan, static_cast<const u32x4 *>(dpacked), static_cast<u32x4 *>(drows));
+    SPD_LAUNCH_CHECK();
+  }
+  const int64_t rows = plan->B * plan->S;
+  hipLaunchKernelGGL(k_zero_unmapped, dim3(row_grid(rows)), dim3(kRowThreads), 0, st, rows, vpr, plan->dst,
+                     plan->counts, static_cast<u32x4 *>(drows));
+  SPD_LAUNCH_CHECK();
+  prof_stop(SPD_K_PACK_ROWS_BWD, st);
   return SPD_OK;
 }
 

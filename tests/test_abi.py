@@ -98,6 +98,18 @@ def test_rows_calls_reject_bad_arguments():
     assert lib.spd_reconstruct(ctypes.byref(p), 5, A[12], 0, A[13], None) == INVALID
     assert lib.spd_reconstruct(ctypes.byref(p), 5, A[12], 48, A[13] + 8, None) == ALIGN
     assert lib.spd_reconstruct(ctypes.byref(p), -1, A[12], 48, A[13], None) == INVALID
+    # backward calls (the zero-fill of pack_rows_bwd launches even for T = 0, so no valid call here)
+    UNSUP = -2
+    assert lib.spd_reconstruct_bwd(ctypes.byref(p), 5, A[12], 24, 1, A[13], None) == ALIGN
+    assert lib.spd_reconstruct_bwd(ctypes.byref(p), 5, A[12], 32, 7, A[13], None) == UNSUP     # dtype
+    assert lib.spd_reconstruct_bwd(ctypes.byref(p), 33, A[12], 32, 1, A[13], None) == INVALID  # T > B*S
+    assert lib.spd_reconstruct_bwd(ctypes.byref(p), 5, None, 32, 1, A[13], None) == INVALID
+    assert lib.spd_reconstruct_bwd(ctypes.byref(p), 5, A[12], 32, 0, A[13] + 4, None) == ALIGN
+    assert lib.spd_reconstruct_bwd(ctypes.byref(p), 0, A[12], 32, 1, A[13], None) == OK       # empty
+    assert lib.spd_pack_rows_bwd(ctypes.byref(p), 5, A[12], 0, A[13], None) == INVALID
+    assert lib.spd_pack_rows_bwd(ctypes.byref(p), 5, A[12] + 8, 32, A[13], None) == ALIGN
+    assert lib.spd_pack_rows_bwd(ctypes.byref(p), -1, A[12], 32, A[13], None) == INVALID
+    assert lib.spd_pack_rows_bwd(ctypes.byref(p), 5, A[12], 32, None, None) == INVALID
 
 
 def _desc(**kw):

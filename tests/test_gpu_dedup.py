@@ -150,3 +150,72 @@ def test_repeat_calls_are_identical():
         assert torch.equal(getattr(a[4].plan, f)[:T], getattr(b[4].plan, f)[:T])
     for f in ("dst", "resp_off", "resp_len", "group_of", "grp_idx"):
         assert torch.equal(getattr(a[4].plan, f), getattr(b[4].plan, f))
+
+
+# ---------------------------------------------------------------- backward of reconstruct / pack_rows
+
+BWD_ROW_CASES = [(SMALL[0], 512), (SMALL[1], 48), (SMALL[2], 32), (SMALL[4], 16),
+                 (WORKLOADS["qwen3_0p6b_2x8_p8192_r512"], 256), (WORKLOADS["redundancy_1x10_p10240_r1024"], 128),
+                 (WORKLOADS["long_2x8_p32768_r256to1024_unpad"], 64), (WORKLOADS["bwd_4x8_p4096_r1024"], 160)]
+
+
+def _bf16_round(a):
+    """float32 -> nearest bfloat16 (ties to even), as float32."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("w,row_bytes", BWD_ROW_CASES, ids=[f"{w.name}-{r}B" for w, r in BWD_ROW_CASES])
+def test_rows_backward(w, row_bytes):
+    """pack_rows_bwd is a byte scatter: bit-exact.  reconstruct_bwd sums each packed row's readers in fp32 and
+    rounds once: within (n - 1) 2^-24 sum|x| (fp32 accumulation of n terms) plus half a bf16 ulp of the exact
+    sum (bf16 keeps 8 significant bits: at most 2^-8 |sum|)."""
+    import shared_prompt_dedup_amd as spd
+    say(f"[rows bwd] {w.name} row_bytes={row_bytes}")
+    bt = make_batch(w, permute=True)
+    groups, _, _, _, oinfo = oracle_plan(bt, w.use_unpad)
+    _, _, _, _, ginfo = gpu_plan(bt, w.use_unpad)
+    rng = np.random.default_rng(9)
+    B, S, T = oinfo["B"], oinfo["S"], oinfo["T"]
+    nmax = max(len(m) for m in groups)
+    # pack_rows backward
+    W = row_bytes // 4
+    dp = rng.integers(-2**31, 2**31 - 1, size=(T, W), dtype=np.int64).astype(np.int32)
+    got = spd.pack_rows_bwd(torch.from_numpy(dp).cuda(), ginfo)
+    np.testing.assert_array_equal(got.cpu().numpy(), oracle.pack_rows_backward(dp, oinfo))
+    del got
+    # reconstruct backward, bf16 and fp32 rows
+    for dt, elt in ((torch.bfloat16, 2), (torch.float32, 4)):
+        W = row_bytes // elt
+        vals = rng.standard_normal((B, S, W)).astype(np.float32)
+        if dt == torch.bfloat16:
+            vals = _bf16_round(vals)
+        got = spd.reconstruct_bwd(torch.from_numpy(vals).to("cuda", dt), ginfo).float().cpu().numpy()
+        ref = oracle.reconstruct_backward(vals, oinfo)
+        absum = oracle.reconstruct_backward(np.abs(vals), oinfo)
+        bound = (nmax - 1) * 2.0**-24 * absum + (2.0**-8 * np.abs(ref) if dt == torch.bfloat16 else 0.0)
+        err = np.abs(got - ref)
+        say(f"  reconstruct_bwd {dt}: max_err={err.max() if err.size else 0:.3e} "
+            f"exact={np.mean(got == (_bf16_round(ref) if dt == torch.bfloat16 else ref.astype(np.float32))):.6f}")
+        assert (err <= bound + 1e-30).all()
+
+
+def test_rows_autograd():
+    """reconstruct_sequences and pack_rows are differentiable through the library's backward calls."""
+    import shared_prompt_dedup_amd as spd
+    w = SMALL[1]
+    bt = make_batch(w, permute=True)
+    _, _, _, _, oinfo = oracle_plan(bt, True)
+    _, _, _, _, ginfo = gpu_plan(bt, True)
+    T, B, S, H = oinfo["T"], oinfo["B"], oinfo["S"], 64
+    x = torch.randn(T, H, dtype=torch.bfloat16, device="cuda", requires_grad=True)
+    gy = torch.randn(B, S, H, dtype=torch.bfloat16, device="cuda")
+    y = spd.reconstruct_sequences(x[None], ginfo)
+    (y * gy).sum().backward()
+    np.testing.assert_array_equal(x.grad.float().cpu().numpy(),
+                                  spd.reconstruct_bwd(gy, ginfo).float().cpu().numpy())
+    ref = oracle.reconstruct_backward(gy.float().cpu().numpy(), oinfo)
+    assert (np.abs(x.grad.float().cpu().numpy() - ref) <= 2.0**-8 * np.abs(ref) + 1e-6).all()
+    rows = torch.randn(B, S, H, dtype=torch.float32, device="cuda", requires_grad=True)
+    gp = torch.randn(T, H, dtype=torch.float32, device="cuda")
+    (spd.pack_rows(rows, ginfo) * gp).sum().backward()
+    np.testing.assert_array_equal(rows.grad.cpu().numpy(), oracle.pack_rows_backward(gp.cpu().numpy(), oinfo))
