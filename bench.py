@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name in workloads.WORKLOADS")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--profile-steps", type=int, default=5, help="steps timed per kernel with HIP events")
+    ap.add_argument("--mode", choices=("split", "standard"), default="split",
+                    help="split attention on the deduplicated batch (default), or the standard QKV mode: the "
+                         "same layer with attention run per sample on the full batch")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -163,7 +166,7 @@ def main():
     hidden = torch.randn((B, S, W), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
     dout_full = torch.randn((B, S, W), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
-    def step():
+    def step_split():
         g, u = spd.group(ids, R, return_lists=False)
         _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=w.use_unpad)
         packed = spd.pack_rows(hidden, inf)
@@ -173,6 +176,32 @@ def main():
         dq, dk, dv = spd.split_attn_bwd(q, k, v, o, lse, dout, inf)
         dhidden = spd.pack_rows_bwd(dq.view(T, W), inf)
         return packed, out, dhidden, dk, dv
+
+    def step_standard():
+        # Standard QKV: Q, K, V reconstructed to the full batch (every sample its own prompt copy), attention
+        # per sample there, output and gradients moved back to the deduplicated layout.
+        g, u = spd.group(ids, R, return_lists=False)
+        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=w.use_unpad)
+        _, _, full = spd.create_full_batch(ids, pos, R, attention_mask=mask, use_unpad=w.use_unpad)
+        packed = spd.pack_rows(hidden, inf)
+        qf, kf, vf = (spd.repack_rows(t, full, inf) for t in (q, k, v))
+        of, lsef = spd.split_attn_fwd(qf, kf, vf, full)
+        o = spd.repack_rows(of, inf, full)
+        out = spd.reconstruct(o.view(T, W), inf)
+        dout = spd.reconstruct_bwd(dout_full, inf)
+        dof = spd.repack_rows_bwd(dout, inf, full).view(-1, Hq, d)
+        dqf, dkf, dvf = spd.split_attn_bwd(qf, kf, vf, of, lsef, dof, full)
+        dq, dk, dv = (spd.repack_rows_bwd(t, full, inf) for t in (dqf, dkf, dvf))
+        dhidden = spd.pack_rows_bwd(dq.view(T, W), inf)
+        return packed, out, dhidden, dk, dv
+
+    step = step_split if args.mode == "split" else step_standard
+    kernel_pairs = pairs
+    if args.mode == "standard":
+        _, _, full0 = spd.create_full_batch(ids, pos, R, attention_mask=mask, use_unpad=w.use_unpad)
+        kernel_pairs = attended_pairs(full0)      # what the full-batch attention evaluates
+        T_full = full0["T"]
+        del full0
 
     for _ in range(args.warmup):
         step()
@@ -195,11 +224,12 @@ def main():
     prof = spd.profile_end()
     kern_ms = {kname: (tot / n if n else None) for kname, (n, tot) in prof.items()}
     row_bytes = W * 2
+    Ta = T if args.mode == "split" else T_full    # rows the attention kernels run on
     kernel_work = {
-        "fwd": ("mfma", 4 * d * Hq * pairs),
-        "bwd_dkdv": ("mfma", 8 * d * Hq * pairs),      # S, dP recomputed; dV, dK
-        "bwd_dq": ("mfma", 6 * d * Hq * pairs),        # S, dP recomputed; dQ
-        "bwd_pre": ("hbm", 2 * T * W * 2 + T * Hq * 4),
+        "fwd": ("mfma", 4 * d * Hq * kernel_pairs),
+        "bwd_dkdv": ("mfma", 8 * d * Hq * kernel_pairs),      # S, dP recomputed; dV, dK
+        "bwd_dq": ("mfma", 6 * d * Hq * kernel_pairs),        # S, dP recomputed; dQ
+        "bwd_pre": ("hbm", 2 * Ta * W * 2 + Ta * Hq * 4),
         "reconstruct": ("hbm", T * row_bytes + B * S * row_bytes),
         "pack_rows": ("hbm", 2 * T * row_bytes),
         "reconstruct_bwd": ("hbm", B * S * row_bytes + T * row_bytes),
@@ -233,7 +263,7 @@ def main():
     dom = max(kernels, key=lambda kk: kernels[kk]["ms"])
     roof = dict(kernels[dom])
     roof.pop("ms")
-    roof = {"kernel": dom, **roof, "traffic": measured_traffic(dom, name)}
+    roof = {"kernel": dom, **roof, "traffic": measured_traffic(dom, name) if args.mode == "split" else None}
 
     attn_ms = sum(kern_ms[kk] for kk in ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv") if kern_ms.get(kk))
     result = {
@@ -251,7 +281,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "batch": B, "unique_prompts": w.num_prompts, "prompt_len": w.prompt_len,
                    "response_len": w.response_len, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
-                   "packed_tokens": T, "attended_pairs": pairs, "parallelism": "single GPU"},
+                   "packed_tokens": T, "attended_pairs": pairs, "parallelism": "single GPU",
+                   "attention": args.mode},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "attention_kernels_tflops": round((fwd_flops + bwd_flops) / (attn_ms * 1e-3) / 1e12, 2),
         "roofline": roof,

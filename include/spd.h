@@ -15,6 +15,10 @@
  *   spd_reconstruct_bwd, spd_pack_rows_bwd
  *                        -- "Correctness & Gradients": gradients flow back
  *                           through the reconstruction and the deduplication
+ *   spd_group_singletons, spd_repack_rows, spd_repack_rows_bwd
+ *                        -- Phase 2, "Standard QKV Optimization": Q, K, V of
+ *                           the deduplicated batch reconstructed to the full
+ *                           batch for standard causal attention
  *
  * Conventions shared by every call
  * --------------------------------
@@ -189,6 +193,44 @@ spd_status spd_reconstruct_bwd(const spd_plan *plan, int64_t T, const void *dout
  */
 spd_status spd_pack_rows_bwd(const spd_plan *plan, int64_t T, const void *dpacked, int64_t row_bytes,
                              void *drows, void *stream);
+
+/*
+ * The plan of the non-deduplicated batch: every sample is its own group
+ * (group_of[b] = rep[b] = b, counts[0] = B), no hashing.  spd_pack with this
+ * plan lays the batch out sample by sample -- each sample's prompt, then its
+ * response -- which is the full batch in variable-length form, and the split
+ * attention calls on it compute standard per-sample causal attention (the
+ * "Standard QKV Optimization" of Phase 2).  Same argument rules as spd_group.
+ */
+spd_status spd_group_singletons(int64_t B, int64_t S, int64_t response_length, const spd_plan *plan,
+                                void *stream);
+
+/*
+ * Moves rows between the packed layouts of two plans of the same batch (same
+ * B, S, P and attention mask):
+ *   out[j, :] = in[from.dst[to.src[j]], :]     (zeros if that cell has no row in "from")
+ * e.g. deduplicated Q -> the full batch (to = singleton plan), or the full
+ * batch's attention output -> the deduplicated layout (to = deduplicated plan;
+ * a prompt row takes the copy of the member it was packed from).
+ *   in         device [T_from, row_bytes] (any element type; copied as bytes).
+ *   out        device [T_to, row_bytes].
+ * row_bytes must be a positive multiple of 16.
+ */
+spd_status spd_repack_rows(const spd_plan *to, int64_t T_to, const spd_plan *from, int64_t T_from,
+                           const void *in, int64_t row_bytes, void *out, void *stream);
+
+/*
+ * Backward of spd_repack_rows (its transpose):
+ *   din[i, :] = sum over rows j of "to" with from.dst[to.src[j]] == i of dout[j, :],
+ * summed in ascending member order in fp32 and rounded once.  From the
+ * deduplicated layout to the full batch, a prompt row collects every member's
+ * copy; from the full batch to the deduplicated layout, only the copy of the
+ * member the prompt row was packed from receives the gradient (others 0).
+ *   dout       device [T_to, row_bytes], elements of type dtype (SPD_F32 or SPD_BF16).
+ *   din        device [T_from, row_bytes], same dtype; every row is written.
+ */
+spd_status spd_repack_rows_bwd(const spd_plan *to, int64_t T_to, const spd_plan *from, int64_t T_from,
+                               const void *dout, int64_t row_bytes, int32_t dtype, void *din, void *stream);
 
 /* ---------------------------------------------------------- split attention */
 

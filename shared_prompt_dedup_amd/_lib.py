@@ -50,6 +50,12 @@ _SIG = {
     "spd_reconstruct_bwd": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, _P, ctypes.c_int64,
                                            ctypes.c_int32, _P, _P]),
     "spd_pack_rows_bwd": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, _P, ctypes.c_int64, _P, _P]),
+    "spd_group_singletons": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(SpdPlan),
+                                            _P]),
+    "spd_repack_rows": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, ctypes.POINTER(SpdPlan),
+                                       ctypes.c_int64, _P, ctypes.c_int64, _P, _P]),
+    "spd_repack_rows_bwd": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, ctypes.POINTER(SpdPlan),
+                                           ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
     "spd_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SpdAttnDesc), ctypes.c_int64, ctypes.c_int64]),
     "spd_split_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SpdAttnDesc), ctypes.POINTER(SpdPlan), ctypes.c_int64,
                                           _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),

@@ -267,6 +267,66 @@ def reconstruct(dedup_hidden: torch.Tensor, info: ReconstructionInfo) -> torch.T
     return Reconstruct.apply(x, info)
 
 
+def singleton_groups(input_ids: torch.Tensor, response_length: int):
+    """spd_group_singletons: every sample its own group (the non-deduplicated batch).
+
+    Returns ``(prompt_groups, prompts [B, P])`` like ``group``."""
+    _need_cuda(input_ids, "input_ids")
+    if input_ids.dtype != torch.int64 or input_ids.dim() != 2:
+        raise ValueError("input_ids must be int64 [batch, seq_len]")
+    B, S = input_ids.shape
+    P = S - int(response_length)
+    plan = Plan(B, S, P, input_ids.device)
+    check("spd_group_singletons", lib.spd_group_singletons(B, S, int(response_length), ctypes.byref(plan.c),
+                                                           _stream(input_ids.device)))
+    plan.G = B
+    return PromptGroups([[b] for b in range(B)], plan), input_ids[:, :P]
+
+
+def create_full_batch(input_ids, position_ids, response_length, attention_mask=None, use_unpad=False):
+    """The full (non-deduplicated) batch in packed variable-length form -- every sample's prompt, then its
+    response: ``(ids [1, T_full], positions [1, T_full], info)``.  Attention on ``info`` is standard per-sample
+    causal attention (Phase 2, Standard QKV Optimization)."""
+    groups, prompts = singleton_groups(input_ids, response_length)
+    return pack(input_ids, position_ids, response_length, groups, prompts, attention_mask, use_unpad)
+
+
+def _row_bytes(x: torch.Tensor) -> int:
+    return (x[0].numel() if x.dim() > 1 else 1) * x.element_size()
+
+
+def repack_rows(x: torch.Tensor, to_info: ReconstructionInfo, from_info: ReconstructionInfo) -> torch.Tensor:
+    """spd_repack_rows: rows of ``from_info``'s packed layout ``[T_from, ...]`` -> ``to_info``'s ``[T_to, ...]``."""
+    to, fr = to_info.plan, from_info.plan
+    _need_cuda(x, "x")
+    if x.shape[0] != fr.T:
+        raise ValueError(f"x has {x.shape[0]} rows, the source layout has T = {fr.T}")
+    out = torch.empty((to.T,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    check("spd_repack_rows", lib.spd_repack_rows(ctypes.byref(to.c), to.T, ctypes.byref(fr.c), fr.T, _ptr(x),
+                                                 _row_bytes(x), _ptr(out), _stream(x.device)))
+    return out
+
+
+def repack_rows_bwd(dout: torch.Tensor, to_info: ReconstructionInfo, from_info: ReconstructionInfo) -> torch.Tensor:
+    """spd_repack_rows_bwd: the transpose of ``repack_rows(., to_info, from_info)``: ``[T_to, ...] -> [T_from, ...]``
+    (fp32 accumulation, one rounding; bf16 or fp32)."""
+    to, fr = to_info.plan, from_info.plan
+    _need_cuda(dout, "dout")
+    if dout.shape[0] != to.T:
+        raise ValueError(f"dout has {dout.shape[0]} rows, the layout has T = {to.T}")
+    if dout.dtype == torch.bfloat16:
+        dt = SPD_BF16
+    elif dout.dtype == torch.float32:
+        dt = SPD_F32
+    else:
+        raise TypeError("repack_rows_bwd supports bfloat16 and float32 gradients")
+    out = torch.empty((fr.T,) + tuple(dout.shape[1:]), dtype=dout.dtype, device=dout.device)
+    check("spd_repack_rows_bwd", lib.spd_repack_rows_bwd(ctypes.byref(to.c), to.T, ctypes.byref(fr.c), fr.T,
+                                                         _ptr(dout), _row_bytes(dout), dt, _ptr(out),
+                                                         _stream(dout.device)))
+    return out
+
+
 # ---------------------------------------------------------------------------- attention
 
 
@@ -352,6 +412,34 @@ class SplitAttention(torch.autograd.Function):
 
 def split_attention(q, k, v, info, softmax_scale=None):
     return SplitAttention.apply(q, k, v, info, softmax_scale)
+
+
+class StandardAttention(torch.autograd.Function):
+    """Phase 2, Standard QKV Optimization: Q, K, V of the deduplicated batch are reconstructed to the full batch
+    (``full_info`` from ``create_full_batch``), standard per-sample causal attention runs there, and the output
+    comes back in the deduplicated layout (each prompt row from the member it was packed from).  The result equals
+    split attention's; the prompt's self-attention is computed once per member instead of once per group."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, info, full_info, softmax_scale=None):
+        qf, kf, vf = (repack_rows(t, full_info, info) for t in (q, k, v))
+        of, lsef = split_attn_fwd(qf, kf, vf, full_info, softmax_scale)
+        ctx.save_for_backward(qf, kf, vf, of, lsef)
+        ctx.info, ctx.full_info, ctx.scale = info, full_info, softmax_scale
+        return repack_rows(of, info, full_info)
+
+    @staticmethod
+    def backward(ctx, do):
+        qf, kf, vf, of, lsef = ctx.saved_tensors
+        info, full = ctx.info, ctx.full_info
+        dof = repack_rows_bwd(do.contiguous(), info, full)
+        dqf, dkf, dvf = split_attn_bwd(qf, kf, vf, of, lsef, dof, full, ctx.scale)
+        return (repack_rows_bwd(dqf, full, info), repack_rows_bwd(dkf, full, info), repack_rows_bwd(dvf, full, info),
+                None, None, None)
+
+
+def standard_attention(q, k, v, info, full_info, softmax_scale=None):
+    return StandardAttention.apply(q, k, v, info, full_info, softmax_scale)
 
 
 # ---------------------------------------------------------------------------- the pages' names

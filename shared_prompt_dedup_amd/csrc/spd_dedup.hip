@@ -353,21 +353,26 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Output rows are written once and not re-read by this kernel: non-temporal.
 __device__ inline void stream_store(u32x4 *p, const u32x4 &v) { __builtin_nontemporal_store(v, p); }
 
+// packed[j] = rows[src[j]]; with cell_row (another plan's dst), the input is
+// that plan's packed layout: packed[j] = rows[cell_row[src[j]]], zeros where
+// the cell has no row there.
 __global__ void __launch_bounds__(kRowThreads) k_pack_rows(int64_t T, int64_t vec_per_row,
                                                             const int32_t *__restrict__ src,
+                                                            const int32_t *__restrict__ cell_row,
                                                             const u32x4 *__restrict__ rows,
                                                             u32x4 *__restrict__ packed) {
   const int lane = __lane_id();
   const int64_t nwaves = int64_t(gridDim.x) * (kRowThreads / 64);
   for (int64_t j = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; j < T; j += nwaves) {
-    const u32x4 *in = rows + int64_t(src[j]) * vec_per_row;
+    const int64_t r = cell_row ? cell_row[src[j]] : src[j];
+    const u32x4 *in = rows + r * vec_per_row;
     u32x4 *out = packed + j * vec_per_row;
     for (int64_t c0 = 0; c0 < vec_per_row; c0 += 64 * kU) {
       u32x4 v[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int64_t c = c0 + u * 64 + lane;
-        if (c < vec_per_row) v[u] = in[c];
+        v[u] = (c < vec_per_row && r >= 0) ? in[c] : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -428,9 +433,15 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
 // every (b, t) that reads it -- for a prompt row, column t of each member of
 // the group, summed in ascending member order in fp32 and rounded once; for a
 // response row, its own (b, t).  E is the element type (bf16 or fp32).
+// With to_dst / to_src (another plan "to"), the gradient of cell (b, t) is the
+// row to_dst[b*S+t] of a [T_to] input, and a cell counts only if it is that
+// row's source (to_src[to_dst[c]] == c): the transpose of
+// out[i] = in[plan.dst[to.src[i]]].
 template <typename E>
 __global__ void __launch_bounds__(kRowThreads) k_reconstruct_bwd(int64_t T, int64_t S, int64_t P,
                                                                   int64_t vec_per_row, spd_plan plan,
+                                                                  const int32_t *__restrict__ to_dst,
+                                                                  const int32_t *__restrict__ to_src,
                                                                   const u32x4 *__restrict__ dout,
                                                                   u32x4 *__restrict__ dpacked) {
   constexpr int EPV = 16 / sizeof(E);   // elements per 16-byte vector
@@ -457,7 +468,13 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct_bwd(int64_t T, int6
         for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
       for (int m = m0; m < m1; ++m) {
         const int64_t b = members ? members[m] : b0;
-        const u32x4 *in = dout + (b * S + t) * vec_per_row;
+        const int64_t cell = b * S + t;
+        int64_t r = cell;
+        if (to_dst) {
+          r = to_dst[cell];
+          if (r < 0 || to_src[r] != cell) continue;
+        }
+        const u32x4 *in = dout + r * vec_per_row;
         u32x4 v[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -480,6 +497,21 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct_bwd(int64_t T, int6
         if (c < vec_per_row) stream_store(o + c, __builtin_bit_cast(u32x4, y));
       }
     }
+  }
+}
+
+// Every sample its own group: the plan of the non-deduplicated batch.
+__global__ void k_singleton_groups(int B, spd_plan plan) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) {
+    plan.group_of[b] = b;
+    plan.grp_idx[b] = b;
+    plan.rep[b] = b;
+    plan.grp_off[b] = b;
+  }
+  if (b == 0) {
+    plan.grp_off[B] = B;
+    plan.counts[0] = B;
   }
 }
 
@@ -597,7 +629,8 @@ extern "C" spd_status spd_pack_rows(const spd_plan *plan, int64_t T, const void 
   hipStream_t st = static_cast<hipStream_t>(stream);
   prof_start(SPD_K_PACK_ROWS, st);
   hipLaunchKernelGGL(k_pack_rows, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, row_bytes / 16, plan->src,
-                     static_cast<const u32x4 *>(rows), static_cast<u32x4 *>(packed));
+                     static_cast<const int32_t *>(nullptr), static_cast<const u32x4 *>(rows),
+                     static_cast<u32x4 *>(packed));
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_PACK_ROWS, st);
   return SPD_OK;
@@ -636,10 +669,12 @@ extern "C" spd_status spd_reconstruct_bwd(const spd_plan *plan, int64_t T, const
   prof_start(SPD_K_RECONSTRUCT_BWD, st);
   if (dtype == SPD_BF16)
     hipLaunchKernelGGL(k_reconstruct_bwd<__bf16>, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, plan->S, plan->P,
-                       vpr, *plan, static_cast<const u32x4 *>(dout), static_cast<u32x4 *>(dpacked));
+                       vpr, *plan, static_cast<const int32_t *>(nullptr), static_cast<const int32_t *>(nullptr),
+                       static_cast<const u32x4 *>(dout), static_cast<u32x4 *>(dpacked));
   else
     hipLaunchKernelGGL(k_reconstruct_bwd<float>, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, plan->S, plan->P,
-                       vpr, *plan, static_cast<const u32x4 *>(dout), static_cast<u32x4 *>(dpacked));
+                       vpr, *plan, static_cast<const int32_t *>(nullptr), static_cast<const int32_t *>(nullptr),
+                       static_cast<const u32x4 *>(dout), static_cast<u32x4 *>(dpacked));
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_RECONSTRUCT_BWD, st);
   return SPD_OK;
@@ -663,6 +698,66 @@ extern "C" spd_status spd_pack_rows_bwd(const spd_plan *plan, int64_t T, const v
                      plan->counts, static_cast<u32x4 *>(drows));
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_PACK_ROWS_BWD, st);
+  return SPD_OK;
+}
+
+extern "C" spd_status spd_group_singletons(int64_t B, int64_t S, int64_t response_length, const spd_plan *plan,
+                                           void *stream) {
+  SPD_TRY(validate_plan(plan));
+  if (B != plan->B || S != plan->S || response_length < 0 || response_length > S ||
+      plan->P != S - response_length)
+    return SPD_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_singleton_groups, dim3((B + 255) / 256), dim3(256), 0, st, int(B), *plan);
+  SPD_LAUNCH_CHECK();
+  return SPD_OK;
+}
+
+namespace {
+spd_status validate_pair(const spd_plan *to, int64_t T_to, const spd_plan *from, int64_t T_from) {
+  SPD_TRY(validate_plan(to));
+  SPD_TRY(validate_plan(from));
+  if (to->B != from->B || to->S != from->S || to->P != from->P) return SPD_ERR_INVALID_ARG;
+  if (T_to < 0 || T_to > to->B * to->S || T_from < 0 || T_from > from->B * from->S) return SPD_ERR_INVALID_ARG;
+  return SPD_OK;
+}
+}  // namespace
+
+extern "C" spd_status spd_repack_rows(const spd_plan *to, int64_t T_to, const spd_plan *from, int64_t T_from,
+                                      const void *in, int64_t row_bytes, void *out, void *stream) {
+  SPD_TRY(validate_pair(to, T_to, from, T_from));
+  if (!in || !out || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if (row_bytes % 16 || !aligned16(in) || !aligned16(out)) return SPD_ERR_ALIGNMENT;
+  if (T_to == 0) return SPD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_pack_rows, dim3(row_grid(T_to)), dim3(kRowThreads), 0, st, T_to, row_bytes / 16, to->src,
+                     static_cast<const int32_t *>(from->dst), static_cast<const u32x4 *>(in),
+                     static_cast<u32x4 *>(out));
+  SPD_LAUNCH_CHECK();
+  return SPD_OK;
+}
+
+extern "C" spd_status spd_repack_rows_bwd(const spd_plan *to, int64_t T_to, const spd_plan *from, int64_t T_from,
+                                          const void *dout, int64_t row_bytes, int32_t dtype, void *din,
+                                          void *stream) {
+  SPD_TRY(validate_pair(to, T_to, from, T_from));
+  if (!dout || !din || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if (dtype != SPD_F32 && dtype != SPD_BF16) return SPD_ERR_UNSUPPORTED;
+  if (row_bytes % 16 || !aligned16(dout) || !aligned16(din)) return SPD_ERR_ALIGNMENT;
+  if (T_from == 0) return SPD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t vpr = row_bytes / 16;
+  if (dtype == SPD_BF16)
+    hipLaunchKernelGGL(k_reconstruct_bwd<__bf16>, dim3(row_grid(T_from)), dim3(kRowThreads), 0, st, T_from,
+                       from->S, from->P, vpr, *from, static_cast<const int32_t *>(to->dst),
+                       static_cast<const int32_t *>(to->src), static_cast<const u32x4 *>(dout),
+                       static_cast<u32x4 *>(din));
+  else
+    hipLaunchKernelGGL(k_reconstruct_bwd<float>, dim3(row_grid(T_from)), dim3(kRowThreads), 0, st, T_from,
+                       from->S, from->P, vpr, *from, static_cast<const int32_t *>(to->dst),
+                       static_cast<const int32_t *>(to->src), static_cast<const u32x4 *>(dout),
+                       static_cast<u32x4 *>(din));
+  SPD_LAUNCH_CHECK();
   return SPD_OK;
 }
 

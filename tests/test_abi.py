@@ -112,6 +112,22 @@ def test_rows_calls_reject_bad_arguments():
     assert lib.spd_pack_rows_bwd(ctypes.byref(p), 5, A[12], 32, None, None) == INVALID
 
 
+def test_standard_mode_calls_reject_bad_arguments():
+    p, q = _plan(), _plan()
+    other = _plan(B=3)
+    assert lib.spd_group_singletons(3, 8, 2, ctypes.byref(p), None) == INVALID     # B mismatch
+    assert lib.spd_group_singletons(4, 8, 3, ctypes.byref(p), None) == INVALID     # P = S - response_length
+    assert lib.spd_repack_rows(ctypes.byref(p), 5, ctypes.byref(other), 5, A[12], 32, A[13], None) == INVALID
+    assert lib.spd_repack_rows(ctypes.byref(p), 33, ctypes.byref(q), 5, A[12], 32, A[13], None) == INVALID
+    assert lib.spd_repack_rows(ctypes.byref(p), 5, ctypes.byref(q), 5, A[12], 24, A[13], None) == ALIGN
+    assert lib.spd_repack_rows(ctypes.byref(p), 5, ctypes.byref(q), 5, None, 32, A[13], None) == INVALID
+    assert lib.spd_repack_rows(ctypes.byref(p), 0, ctypes.byref(q), 5, A[12], 32, A[13], None) == OK   # empty
+    assert lib.spd_repack_rows_bwd(ctypes.byref(p), 5, ctypes.byref(q), 5, A[12], 32, 9, A[13], None) == UNSUPPORTED
+    assert lib.spd_repack_rows_bwd(ctypes.byref(p), 5, ctypes.byref(other), 5, A[12], 32, 1, A[13], None) == INVALID
+    assert lib.spd_repack_rows_bwd(ctypes.byref(p), 5, ctypes.byref(q), 5, A[12], 32, 1, A[13] + 2, None) == ALIGN
+    assert lib.spd_repack_rows_bwd(ctypes.byref(p), 5, ctypes.byref(q), 0, A[12], 32, 1, A[13], None) == OK
+
+
 def _desc(**kw):
     d = dict(num_q_heads=16, num_kv_heads=8, head_dim=128, dtype=1, softmax_scale=0.088)
     d.update(kw)

@@ -315,3 +315,20 @@ def test_planted_mistake_in_reconstruct_backward_is_caught():
     y = rng.standard_normal((w.batch, w.seq_len, 3))
     gap, scale = _adjoint_gap(lambda a: oracle.reconstruct_sequences(a, info), lambda a: wrong(a, info), x, y)
     assert gap > 1e-3 * scale
+
+
+@pytest.mark.parametrize("use_unpad", [False, True])
+def test_full_batch_layout_is_samples_concatenated(use_unpad):
+    """Standard QKV Optimization: with every sample its own group the packed layout is the full batch,
+    sample after sample, each its kept prompt then its kept response tokens."""
+    w = WORKLOADS["tiny_fp32"].scaled(resp_len_range=(0, 32))
+    bt = make_batch(w, permute=True)
+    P = w.prompt_len
+    groups = [[b] for b in range(w.batch)]
+    ids, pos, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups,
+                                                      bt.input_ids[:, :P], attention_mask=bt.attention_mask,
+                                                      use_unpad=use_unpad)
+    keep = bt.attention_mask != 0 if use_unpad else np.ones(bt.input_ids.shape, bool)
+    np.testing.assert_array_equal(np.asarray(ids).ravel(), bt.input_ids[keep])
+    np.testing.assert_array_equal(np.asarray(pos).ravel(), bt.position_ids[keep])
+    assert info["T"] == keep.sum()
