@@ -88,26 +88,43 @@ def _prep(q, k, v, scale):
     return q, k, v, T, Hq, Hkv, d, float(scale)
 
 
+def _sample_seq(info, b, valid):
+    """Packed rows of sample ``b``'s sequence and how many of them are prompt rows.
+
+    With ``valid`` (bool per packed row; Working with Packed/Unpacked
+    Sequences, padded format with an attention mask) the pads are left out of
+    the sequence: they are no sample's keys or queries, so their outputs and
+    gradients stay 0.
+    """
+    g = info["group_of"][b]
+    pl = int(info["prompt_len"][g])
+    idx = sample_rows(info, b)
+    if valid is None:
+        return idx, pl
+    keep = np.asarray(valid, dtype=bool)[idx]
+    return idx[keep], int(keep[:pl].sum())
+
+
 def _members_rep_first(info, g):
     r = int(info["rep"][g])
     return [r] + [b for b in info["groups"][g] if b != r]
 
 
-def split_attention_forward(q, k, v, info, scale=None, heads=None):
+def split_attention_forward(q, k, v, info, scale=None, heads=None, valid=None):
     """Split attention forward over packed ``q [T,Hq,d]``, ``k, v [T,Hkv,d]``.
 
     Returns ``o [T,Hq,d]`` and ``lse [Hq,T]`` (fp64).  ``heads`` restricts
-    the work to some query heads (others are left 0).
+    the work to some query heads (others are left 0).  ``valid`` (bool [T])
+    marks pads kept in a padded-format batch: they take no part (output 0).
     """
     q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
     heads = range(Hq) if heads is None else heads
     o = np.zeros((T, Hq, d))
     lse = np.zeros((Hq, T))
     for g in range(info["G"]):
-        pl = int(info["prompt_len"][g])
         rep = int(info["rep"][g])
         for b in _members_rep_first(info, g):
-            idx = sample_rows(info, b)
+            idx, pl = _sample_seq(info, b, valid)
             L = len(idx)
             for h in heads:
                 j = _kv_head(h, Hq, Hkv)
@@ -129,13 +146,14 @@ def split_attention_forward(q, k, v, info, scale=None, heads=None):
     return o, lse
 
 
-def split_attention_backward(q, k, v, dout, info, scale=None, heads=None):
+def split_attention_backward(q, k, v, dout, info, scale=None, heads=None, valid=None):
     """Gradients ``(dq, dk, dv)`` of the packed split-attention output.
 
     Per sample: textbook causal-attention backward with that sample's
     ``dO`` (see the module docstring), then scatter-add onto packed rows;
     query heads sharing a kv head add into it.  ``heads`` restricts the work
-    to some query heads (the others contribute nothing).
+    to some query heads (the others contribute nothing).  ``valid`` as in
+    the forward: pads get zero gradients.
     """
     q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
     dout = np.asarray(dout, dtype=np.float64)
@@ -144,10 +162,9 @@ def split_attention_backward(q, k, v, dout, info, scale=None, heads=None):
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for g in range(info["G"]):
-        pl = int(info["prompt_len"][g])
         rep = int(info["rep"][g])
         for b in _members_rep_first(info, g):
-            idx = sample_rows(info, b)
+            idx, pl = _sample_seq(info, b, valid)
             L = len(idx)
             for h in heads:
                 j = _kv_head(h, Hq, Hkv)

@@ -286,3 +286,100 @@ def test_planted_prompt_grad_mistake_is_caught(monkeypatch):
     with pytest.raises(AssertionError):
         test_backward_matches_autograd("tiny")
     assert real is not doubled
+
+
+# ---------------------------------------------------------------- padded format with an attention mask
+# Working with Packed/Unpacked Sequences: in the padded format the pads stay
+# in the packed sequence; the reading here is that they take no part in
+# attention (no sample's key; their outputs and gradients are 0).
+
+def _padded_with_mask(seed=81):
+    w = SMALL["gqa_ragged_unpad"].scaled(seed=seed)
+    bt = make_batch(w, permute=True)
+    mask = bt.attention_mask.copy()
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    mask[groups[0], :4] = 0          # left pads on group 0's prompt (every member)
+    _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
+                                                  attention_mask=mask, use_unpad=False)
+    x = make_attn_inputs(w, info["T"])
+    valid = mask.reshape(-1)[info["src"]] != 0
+    return w, bt, mask, groups, uniq, info, x, valid
+
+
+def _sdpa_packed_masked(q, k, v, info, scale, valid):
+    """Per sample: SDPA over all its rows with keys masked to (key <= query) and valid, for its valid query
+    rows; pad rows are 0."""
+    T, Hq, d = q.shape
+    ratio = Hq // k.shape[1]
+    rows = [None] * T
+    for b in range(info["B"]):
+        idx = np.asarray(oracle.sample_rows(info, b))
+        g = info["group_of"][b]
+        pl = int(info["prompt_len"][g])
+        L = len(idx)
+        vk = torch.as_tensor(valid[idx])
+        allowed = torch.tril(torch.ones(L, L, dtype=torch.bool)) & vk[None, :]
+        qrows = np.nonzero(valid[idx])[0]
+        if len(qrows) == 0:
+            continue
+        ti = torch.as_tensor(idx)
+        Q = q[ti[qrows]].transpose(0, 1)
+        K = k[ti].repeat_interleave(ratio, dim=1).transpose(0, 1)
+        V = v[ti].repeat_interleave(ratio, dim=1).transpose(0, 1)
+        ob = F.scaled_dot_product_attention(Q, K, V, attn_mask=allowed[qrows], scale=scale).transpose(0, 1)
+        for n, i in enumerate(qrows.tolist()):
+            if i >= pl or b == info["rep"][g]:
+                rows[idx[i]] = ob[n]
+    zero = torch.zeros((Hq, d), dtype=q.dtype)
+    return torch.stack([r if r is not None else zero for r in rows])
+
+
+def test_padded_with_mask_matches_library_sdpa():
+    w, bt, mask, groups, uniq, info, x, valid = _padded_with_mask()
+    assert (~valid).sum() > 4          # pads in prompts and responses
+    scale = 1.0 / math.sqrt(w.head_dim)
+    o, _ = oracle.split_attention_forward(x.q, x.k, x.v, info, valid=valid)
+    ref = _sdpa_packed_masked(*(torch.from_numpy(a.astype(np.float64)) for a in (x.q, x.k, x.v)), info, scale, valid)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    assert not o[~valid].any()
+
+
+def test_padded_with_mask_backward_matches_autograd():
+    w, bt, mask, groups, uniq, info, x, valid = _padded_with_mask()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    q, k, v = (torch.from_numpy(a.astype(np.float64)).requires_grad_() for a in (x.q, x.k, x.v))
+    out = _sdpa_packed_masked(q, k, v, info, scale, valid)
+    (out * torch.from_numpy(x.do.astype(np.float64))).sum().backward()
+    dq, dk, dv = oracle.split_attention_backward(x.q, x.k, x.v, x.do, info, valid=valid)
+    for got, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-11)
+    for gr in (dq, dk, dv):
+        assert not gr[~valid].any()
+
+
+def test_padded_with_mask_equals_unpadded():
+    """The valid rows of the padded format give what the unpadded format gives for the same tokens."""
+    w, bt, mask, groups, uniq, info, x, valid = _padded_with_mask()
+    _, _, info_u = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
+                                                    attention_mask=mask, use_unpad=True)
+    rows = np.nonzero(valid)[0]
+    urows = np.asarray(info_u["dst"])[np.asarray(info["src"])[rows]]
+    assert (urows >= 0).all() and len(urows) == info_u["T"]
+    order = np.argsort(urows)
+    src_rows = rows[order]                   # padded row of each unpadded row
+    o, _ = oracle.split_attention_forward(x.q, x.k, x.v, info, valid=valid)
+    ou, _ = oracle.split_attention_forward(x.q[src_rows], x.k[src_rows], x.v[src_rows], info_u)
+    np.testing.assert_allclose(o[src_rows], ou, rtol=0, atol=1e-12)
+    g = oracle.split_attention_backward(x.q, x.k, x.v, x.do, info, valid=valid)
+    gu = oracle.split_attention_backward(x.q[src_rows], x.k[src_rows], x.v[src_rows], x.do[src_rows], info_u)
+    for a, b in zip(g, gu):
+        np.testing.assert_allclose(a[src_rows], b, rtol=0, atol=1e-11)
+
+
+def test_planted_pad_key_leak_is_caught():
+    """Treating the kept pads as keys (ignoring the mask) disagrees with the masked library pin."""
+    w, bt, mask, groups, uniq, info, x, valid = _padded_with_mask()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    wrong, _ = oracle.split_attention_forward(x.q, x.k, x.v, info)
+    ref = _sdpa_packed_masked(*(torch.from_numpy(a.astype(np.float64)) for a in (x.q, x.k, x.v)), info, scale, valid)
+    assert np.abs(wrong[valid] - ref.numpy()[valid]).max() > 1e-3
