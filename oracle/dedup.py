@@ -199,6 +199,76 @@ def pack_rows_backward(dpacked, info):
     return out.reshape((B, S) + x.shape[1:])
 
 
+def attention_mask_to_flash_attn_params(mask):
+    """Flash Attention Integration: a ``[total_q, total_kv]`` block-diagonal
+    attention mask -> variable-length parameters ``cu_seqlens_q``,
+    ``cu_seqlens_k``, ``max_seqlen_q``, ``max_seqlen_k``.
+
+    Readings: block ``i`` owns query rows ``[cu_q[i], cu_q[i+1])`` and key
+    columns ``[cu_k[i], cu_k[i+1])``.  A row's block is named by its first
+    visible key; a row that sees no key belongs to the block of the next row
+    that sees one (bottom-right aligned causal blocks with more queries than
+    keys start with such rows), trailing ones to the last block.  The last
+    key boundary is one past the last visible key.  ``mismatched_rows``
+    counts rows whose visible keys leave their block's range (0 for a
+    block-diagonal mask).
+    """
+    m = np.asarray(mask) != 0
+    Tq = m.shape[0]
+    first, last = [], []
+    for r in range(Tq):
+        nz = np.flatnonzero(m[r])
+        first.append(int(nz[0]) if len(nz) else None)
+        last.append(int(nz[-1]) + 1 if len(nz) else None)
+    owner = [None] * Tq          # first visible key of the row's block
+    nxt = None
+    for r in range(Tq - 1, -1, -1):
+        if first[r] is not None:
+            nxt = first[r]
+        owner[r] = nxt
+    cu_q, cu_k = [], []
+    for r in range(Tq):
+        if owner[r] is not None and (not cu_k or owner[r] != cu_k[-1]):
+            cu_q.append(r)
+            cu_k.append(owner[r])
+    n = len(cu_q)
+    if n == 0:
+        return dict(cu_seqlens_q=np.zeros(1, np.int32), cu_seqlens_k=np.zeros(1, np.int32), max_seqlen_q=0,
+                    max_seqlen_k=0, num_seqs=0, mismatched_rows=0)
+    cu_q.append(Tq)
+    cu_k.append(max(x for x in last if x is not None))
+    bad = 0
+    for i in range(n):
+        for r in range(cu_q[i], cu_q[i + 1]):
+            if first[r] is not None and (first[r] != cu_k[i] or last[r] > cu_k[i + 1]):
+                bad += 1
+    cu_q = np.asarray(cu_q, np.int32)
+    cu_k = np.asarray(cu_k, np.int32)
+    return dict(cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, max_seqlen_q=int(np.diff(cu_q).max()),
+                max_seqlen_k=int(np.diff(cu_k).max()), num_seqs=n, mismatched_rows=bad)
+
+
+def varlen_params(info):
+    """Variable-length parameters of the two attention calls of Phase 2 (Split
+    Attention Optimization) for a packed batch:
+
+    * prompt-to-prompt: ``cu_seqlens`` over the unique prompts (queries and
+      keys alike), ``[G + 1]``;
+    * response-to-full: queries are each sample's response rows
+      (``cu_seqlens_q [B + 1]``), keys each sample's prompt followed by its
+      response (``cu_seqlens_k [B + 1]``, the full batch laid out sample by
+      sample).
+    """
+    pl = np.asarray(info["prompt_len"], np.int64)
+    rl = np.asarray(info["resp_len"], np.int64)
+    gof = np.asarray(info["group_of"], np.int64)
+    kl = pl[gof] + rl
+    cu = lambda a: np.concatenate([[0], np.cumsum(a)]).astype(np.int32)
+    return dict(cu_seqlens_prompt=cu(pl), max_seqlen_prompt=int(pl.max(initial=0)),
+                cu_seqlens_q=cu(rl), cu_seqlens_k=cu(kl), max_seqlen_q=int(rl.max(initial=0)),
+                max_seqlen_k=int(kl.max(initial=0)))
+
+
 def sample_rows(info, b):
     """Packed rows of sample ``b``'s own sequence: its group's prompt, then its response.
 

@@ -332,3 +332,85 @@ def test_full_batch_layout_is_samples_concatenated(use_unpad):
     np.testing.assert_array_equal(np.asarray(ids).ravel(), bt.input_ids[keep])
     np.testing.assert_array_equal(np.asarray(pos).ravel(), bt.position_ids[keep])
     assert info["T"] == keep.sum()
+
+
+# ---------------------------------------------------------------- Flash Attention Integration: varlen parameters
+
+def _block_mask(q_lens, k_lens, style, rng):
+    Tq, Tk = sum(q_lens), sum(k_lens)
+    m = np.zeros((Tq, Tk), bool)
+    r0 = c0 = 0
+    for ql, kl in zip(q_lens, k_lens):
+        for i in range(ql):
+            if style == "full":
+                hi = kl
+            elif style == "causal":            # top-left aligned
+                hi = min(kl, i + 1)
+            else:                              # bottom-right aligned: the last query sees every key
+                hi = kl - ql + i + 1
+            if hi > 0:
+                m[r0 + i, c0:c0 + hi] = True
+        r0, c0 = r0 + ql, c0 + kl
+    return m
+
+
+@pytest.mark.parametrize("style", ["full", "causal", "bottom_right"])
+def test_mask_to_flash_params_round_trip(style):
+    rng = np.random.default_rng(31)
+    for _ in range(5):
+        n = int(rng.integers(1, 7))
+        k_lens = rng.integers(1, 12, n).tolist()
+        q_lens = rng.integers(1, 12, n).tolist()
+        if style == "causal":
+            # square blocks: with fewer queries than keys no query would see the last block's trailing keys,
+            # and the mask could not fix that block's key length
+            q_lens = list(k_lens)
+        p = oracle.attention_mask_to_flash_attn_params(_block_mask(q_lens, k_lens, style, rng))
+        np.testing.assert_array_equal(p["cu_seqlens_q"], np.concatenate([[0], np.cumsum(q_lens)]))
+        np.testing.assert_array_equal(p["cu_seqlens_k"], np.concatenate([[0], np.cumsum(k_lens)]))
+        assert p["max_seqlen_q"] == max(q_lens) and p["max_seqlen_k"] == max(k_lens)
+        assert p["num_seqs"] == n and p["mismatched_rows"] == 0
+
+
+def test_varlen_params_match_the_masks_of_the_two_calls():
+    """Prompt-to-prompt and response-to-full masks built from the plan's definition convert to varlen_params."""
+    w = WORKLOADS["tiny_fp32"].scaled(num_prompts=3, rollout_n=3, resp_len_range=(1, 32), seed=41)
+    bt = make_batch(w, permute=True)
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
+                                                  attention_mask=bt.attention_mask, use_unpad=True)
+    vp = oracle.varlen_params(info)
+    pl, rl, gof = info["prompt_len"], info["resp_len"], info["group_of"]
+    # prompt-to-prompt: each prompt causally over itself
+    tot = int(sum(pl))
+    mp = np.zeros((tot, tot), bool)
+    o = 0
+    for g in range(info["G"]):
+        for i in range(pl[g]):
+            mp[o + i, o:o + i + 1] = True
+        o += pl[g]
+    p = oracle.attention_mask_to_flash_attn_params(mp)
+    np.testing.assert_array_equal(p["cu_seqlens_q"], vp["cu_seqlens_prompt"])
+    np.testing.assert_array_equal(p["cu_seqlens_k"], vp["cu_seqlens_prompt"])
+    # response-to-full: response row i of sample b sees its prompt and its own keys 0..i
+    Tq, Tk = int(sum(rl)), int(sum(pl[gof[b]] + rl[b] for b in range(info["B"])))
+    mr = np.zeros((Tq, Tk), bool)
+    qo = ko = 0
+    for b in range(info["B"]):
+        P = pl[gof[b]]
+        for i in range(rl[b]):
+            mr[qo + i, ko:ko + P + i + 1] = True
+        qo, ko = qo + rl[b], ko + P + rl[b]
+    p = oracle.attention_mask_to_flash_attn_params(mr)
+    np.testing.assert_array_equal(p["cu_seqlens_q"], vp["cu_seqlens_q"])
+    np.testing.assert_array_equal(p["cu_seqlens_k"], vp["cu_seqlens_k"])
+    assert p["max_seqlen_q"] == vp["max_seqlen_q"] and p["max_seqlen_k"] == vp["max_seqlen_k"]
+    assert vp["cu_seqlens_k"][-1] == sum(pl[gof[b]] + rl[b] for b in range(info["B"]))
+
+
+def test_mask_to_flash_params_reports_non_block_masks():
+    m = _block_mask([3, 3], [4, 4], "full", None)
+    m[4, 1] = True                    # a row of block 1 also sees a key of block 0
+    assert oracle.attention_mask_to_flash_attn_params(m)["mismatched_rows"] >= 1
+    p = oracle.attention_mask_to_flash_attn_params(np.zeros((3, 5), bool))
+    assert p["num_seqs"] == 0 and p["cu_seqlens_q"].tolist() == [0]
