@@ -19,6 +19,9 @@
  *                        -- Phase 2, "Standard QKV Optimization": Q, K, V of
  *                           the deduplicated batch reconstructed to the full
  *                           batch for standard causal attention
+ *   spd_mask_to_varlen, spd_varlen_params
+ *                        -- "Flash Attention Integration": variable-length
+ *                           (cu_seqlens) parameters
  *
  * Conventions shared by every call
  * --------------------------------
@@ -90,7 +93,9 @@ typedef struct spd_plan {
   int32_t *src;         /* [B * S] capacity; packed row j -> b * S + t (first T used) */
   int32_t *dst;         /* [B * S] (b, t) -> packed row, or -1 if no packed token maps */
   int32_t *seg_start;   /* [B * S] capacity; first packed row of j's segment */
-  int32_t *counts;      /* [4]     counts[0] = G, counts[1] = T, [2..3] reserved */
+  int32_t *counts;      /* [4]     counts[0] = G, counts[1] = T, counts[2] = batch cells mapped to
+                                     no packed row (unpad mode), counts[3] = packed rows whose
+                                     attention-mask entry is 0 (padded mode with a mask) */
 } spd_plan;
 
 /* ---------------------------------------------------------------- grouping */
@@ -136,8 +141,10 @@ size_t spd_pack_workspace_bytes(int64_t B, int64_t S);
  *                            Format"); 0: keep every token.
  *   dedup_ids, dedup_pos     device int64 with capacity B * S; the first T
  *                            entries receive the packed ids and positions.
- * Writes prompt_off, prompt_len, resp_off, resp_len, src, dst, seg_start and
- * counts[1] = T.
+ * Writes prompt_off, prompt_len, resp_off, resp_len, src, dst, seg_start,
+ * counts[1] = T, counts[2] (cells left out by unpad) and counts[3] (packed
+ * rows whose mask entry is 0: padded mode with a mask keeps such pads in the
+ * packed sequence; attention must then treat them as absent).
  */
 spd_status spd_pack(const int64_t *input_ids, const int64_t *position_ids,
                     const void *attention_mask, int32_t mask_elem_bytes, int32_t use_unpad,
@@ -231,6 +238,49 @@ spd_status spd_repack_rows(const spd_plan *to, int64_t T_to, const spd_plan *fro
  */
 spd_status spd_repack_rows_bwd(const spd_plan *to, int64_t T_to, const spd_plan *from, int64_t T_from,
                                const void *dout, int64_t row_bytes, int32_t dtype, void *din, void *stream);
+
+/* ------------------------------------------------- variable-length parameters */
+
+/* Workspace bytes of spd_mask_to_varlen for total_q query rows. */
+size_t spd_mask_varlen_workspace_bytes(int64_t total_q);
+
+/*
+ * "Flash Attention Integration": a block-diagonal [total_q, total_kv] attention
+ * mask (row = query, column = key, non-zero = visible) -> cu_seqlens.  Block i
+ * owns query rows [cu_seqlens_q[i], cu_seqlens_q[i+1]) and keys
+ * [cu_seqlens_k[i], cu_seqlens_k[i+1]).  A row's block is named by its first
+ * visible key; a row that sees no key belongs to the block of the next row
+ * that sees one (trailing ones to the last block); the last key boundary is
+ * one past the last visible key.
+ *   mask             device [total_q, total_kv], elements of mask_elem_bytes
+ *                    (1, 2, 4 or 8) bytes; row-major, contiguous.
+ *   cu_seqlens_q/k   device int32 [total_q + 1]; entries 0..num_seqs written.
+ *   stats            device int32 [4]: num_seqs, max_seqlen_q, max_seqlen_k,
+ *                    and the number of rows whose visible keys leave their
+ *                    block's range (0 for a block-diagonal mask; the caller
+ *                    decides whether that is an error).
+ * total_q < 2^31 and total_kv * mask_elem_bytes < 2^31, else
+ * SPD_ERR_UNSUPPORTED.
+ */
+spd_status spd_mask_to_varlen(const void *mask, int32_t mask_elem_bytes, int64_t total_q, int64_t total_kv,
+                              int32_t *cu_seqlens_q, int32_t *cu_seqlens_k, int32_t *stats, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
+ * The variable-length parameters of the two attention calls of Phase 2
+ * ("Split Attention Optimization") for a packed batch:
+ *   cu_seqlens_prompt  device int32 [B + 1]; entries 0..G: prompt-to-prompt,
+ *                      over the unique prompts (queries and keys alike).
+ *   cu_seqlens_q       device int32 [B + 1]: response-to-full queries, each
+ *                      sample's response rows.
+ *   cu_seqlens_k       device int32 [B + 1]: response-to-full keys, each
+ *                      sample's prompt followed by its response (the full
+ *                      batch laid out sample by sample).
+ *   max_seqlens        device int32 [3]: longest prompt, response, prompt +
+ *                      response.
+ */
+spd_status spd_varlen_params(const spd_plan *plan, int32_t *cu_seqlens_prompt, int32_t *cu_seqlens_q,
+                             int32_t *cu_seqlens_k, int32_t *max_seqlens, void *stream);
 
 /* ---------------------------------------------------------- split attention */
 

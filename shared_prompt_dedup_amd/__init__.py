@@ -13,7 +13,8 @@ _API = ("Plan", "PromptGroups", "ReconstructionInfo", "SplitAttention", "PackRow
         "create_deduplicated_batch", "find_prompt_groups", "group", "pack", "pack_rows", "pack_rows_bwd",
         "reconstruct", "reconstruct_bwd", "reconstruct_sequences", "split_attention", "split_attn_bwd",
         "split_attn_fwd", "profile_begin", "profile_end", "singleton_groups", "create_full_batch", "repack_rows",
-        "repack_rows_bwd", "StandardAttention", "standard_attention")
+        "repack_rows_bwd", "StandardAttention", "standard_attention", "attention_mask_to_flash_attn_params",
+        "flash_attn_params")
 _LIB = ("EXPORTED", "LIB_PATH", "SpdError")
 
 __all__ = list(_API + _LIB)

@@ -56,6 +56,10 @@ _SIG = {
                                        ctypes.c_int64, _P, ctypes.c_int64, _P, _P]),
     "spd_repack_rows_bwd": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, ctypes.POINTER(SpdPlan),
                                            ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
+    "spd_mask_varlen_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64]),
+    "spd_mask_to_varlen": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
+    "spd_varlen_params": (ctypes.c_int, [ctypes.POINTER(SpdPlan), _P, _P, _P, _P, _P]),
     "spd_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SpdAttnDesc), ctypes.c_int64, ctypes.c_int64]),
     "spd_split_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SpdAttnDesc), ctypes.POINTER(SpdPlan), ctypes.c_int64,
                                           _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),

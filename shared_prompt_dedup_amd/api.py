@@ -66,6 +66,7 @@ class Plan:
         self.G: Optional[int] = None
         self.T: Optional[int] = None
         self.use_unpad = False
+        self.kept_pads = 0
         self._c = SpdPlan(self.B, self.S, self.P, *[t.data_ptr() for t in
                                                     (getattr(self, f) for f in _PLAN_FIELDS)])
 
@@ -76,6 +77,7 @@ class Plan:
     def read_counts(self):
         c = self.counts.cpu().tolist()
         self.G, self.T = int(c[0]), int(c[1])
+        self.kept_pads = int(c[3])
         return self.G, self.T
 
 
@@ -93,8 +95,12 @@ class ReconstructionInfo(dict):
 
     def __init__(self, plan: Plan):
         super().__init__({f: getattr(plan, f) for f in _PLAN_FIELDS})
-        self.update(B=plan.B, S=plan.S, P=plan.P, G=plan.G, T=plan.T, use_unpad=plan.use_unpad)
+        self.update(B=plan.B, S=plan.S, P=plan.P, G=plan.G, T=plan.T, use_unpad=plan.use_unpad,
+                    kept_pads=plan.kept_pads)
         self.plan = plan
+        # Padded format with pads in the packed sequence: the same batch packed without them (same groups).
+        # Attention runs there, pads taking no part (Working with Packed/Unpacked Sequences).
+        self.unpadded: Optional["ReconstructionInfo"] = None
 
 
 # ---------------------------------------------------------------------------- group / pack
@@ -162,7 +168,20 @@ def pack(input_ids: torch.Tensor, position_ids: torch.Tensor, response_length: i
     plan.use_unpad = bool(use_unpad)
     plan.read_counts()
     T = plan.T
-    return dids[:T].view(1, T), dpos[:T].view(1, T), ReconstructionInfo(plan)
+    info = ReconstructionInfo(plan)
+    if not use_unpad and plan.kept_pads > 0:
+        twin = Plan(plan.B, plan.S, plan.P, dev)
+        for f in ("group_of", "grp_off", "grp_idx", "rep"):
+            getattr(twin, f).copy_(getattr(plan, f))
+        twin.counts[:1].copy_(plan.counts[:1])
+        tids = torch.empty(n, dtype=torch.int64, device=dev)
+        tpos = torch.empty(n, dtype=torch.int64, device=dev)
+        check("spd_pack", lib.spd_pack(_ptr(input_ids), _ptr(position_ids), mask_ptr, esz, 1, ctypes.byref(twin.c),
+                                       _ptr(tids), _ptr(tpos), _ptr(ws), ws.numel(), _stream(dev)))
+        twin.use_unpad = True
+        twin.read_counts()
+        info.unpadded = ReconstructionInfo(twin)
+    return dids[:T].view(1, T), dpos[:T].view(1, T), info
 
 
 def _pack_rows(rows: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
@@ -327,6 +346,47 @@ def repack_rows_bwd(dout: torch.Tensor, to_info: ReconstructionInfo, from_info: 
     return out
 
 
+# ---------------------------------------------------------------------------- varlen parameters
+
+
+def attention_mask_to_flash_attn_params(attention_mask: torch.Tensor) -> dict:
+    """Flash Attention Integration: block-diagonal ``[total_q, total_kv]`` mask -> ``cu_seqlens_q``,
+    ``cu_seqlens_k`` (device int32), ``max_seqlen_q``, ``max_seqlen_k``, plus ``num_seqs`` and
+    ``mismatched_rows`` (rows whose visible keys leave their block; 0 for a block-diagonal mask)."""
+    _need_cuda(attention_mask, "attention_mask")
+    if attention_mask.dim() != 2:
+        raise ValueError("attention_mask must be [total_q, total_kv]")
+    m = attention_mask.contiguous()
+    Tq, Tk = m.shape
+    dev = m.device
+    cu_q = torch.empty(Tq + 1, dtype=torch.int32, device=dev)
+    cu_k = torch.empty(Tq + 1, dtype=torch.int32, device=dev)
+    stats = torch.empty(4, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, lib.spd_mask_varlen_workspace_bytes(Tq)), dtype=torch.uint8, device=dev)
+    check("spd_mask_to_varlen", lib.spd_mask_to_varlen(_ptr(m), m.element_size(), Tq, Tk, _ptr(cu_q), _ptr(cu_k),
+                                                       _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)))
+    n, mq, mk, bad = stats.cpu().tolist()
+    return dict(cu_seqlens_q=cu_q[:n + 1], cu_seqlens_k=cu_k[:n + 1], max_seqlen_q=mq, max_seqlen_k=mk,
+                num_seqs=n, mismatched_rows=bad)
+
+
+def flash_attn_params(info: ReconstructionInfo) -> dict:
+    """spd_varlen_params: cu_seqlens of the two Phase 2 attention calls for a packed batch --
+    ``cu_seqlens_prompt`` (prompt-to-prompt), ``cu_seqlens_q`` / ``cu_seqlens_k`` (response-to-full: each sample's
+    response rows against its prompt + response) and the three maxima."""
+    plan = info.plan
+    dev = plan.device
+    cp = torch.empty(plan.B + 1, dtype=torch.int32, device=dev)
+    cq = torch.empty(plan.B + 1, dtype=torch.int32, device=dev)
+    ck = torch.empty(plan.B + 1, dtype=torch.int32, device=dev)
+    mx = torch.empty(3, dtype=torch.int32, device=dev)
+    check("spd_varlen_params", lib.spd_varlen_params(ctypes.byref(plan.c), _ptr(cp), _ptr(cq), _ptr(ck), _ptr(mx),
+                                                     _stream(dev)))
+    m = mx.cpu().tolist()
+    return dict(cu_seqlens_prompt=cp[:plan.G + 1], max_seqlen_prompt=m[0], cu_seqlens_q=cq, cu_seqlens_k=ck,
+                max_seqlen_q=m[1], max_seqlen_k=m[2])
+
+
 # ---------------------------------------------------------------------------- attention
 
 
@@ -353,7 +413,19 @@ def _attn_ws(desc: SpdAttnDesc, plan: Plan, T: int, device):
 
 def split_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, info: ReconstructionInfo,
                    softmax_scale: Optional[float] = None):
-    """spd_split_attn_fwd: packed ``q [T,Hq,d]``, ``k, v [T,Hkv,d]`` -> ``(o, lse [Hq,T])``."""
+    """spd_split_attn_fwd: packed ``q [T,Hq,d]``, ``k, v [T,Hkv,d]`` -> ``(o, lse [Hq,T])``.
+
+    For a padded-format plan that kept pads (``info.unpadded`` set), the rows move to the unpadded layout, the
+    attention runs there and ``o`` comes back with zeros on the pads; ``lse`` is then in the unpadded layout
+    (``[Hq, info.unpadded["T"]]``), as ``split_attn_bwd`` expects it."""
+    u = info.unpadded
+    if u is not None:
+        ou, lse = _attn_fwd(*(repack_rows(t, u, info) for t in (q, k, v)), u, softmax_scale)
+        return repack_rows(ou, info, u), lse
+    return _attn_fwd(q, k, v, info, softmax_scale)
+
+
+def _attn_fwd(q, k, v, info, softmax_scale):
     plan = info.plan
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_cuda(t, name)
@@ -373,7 +445,17 @@ def split_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, info: Reco
 
 
 def split_attn_bwd(q, k, v, o, lse, dout, info: ReconstructionInfo, softmax_scale: Optional[float] = None):
-    """spd_split_attn_bwd: ``(dq, dk, dv)`` from the forward's ``o``, ``lse`` and ``dout``."""
+    """spd_split_attn_bwd: ``(dq, dk, dv)`` from the forward's ``o``, ``lse`` and ``dout`` (for a padded-format
+    plan that kept pads, computed in the unpadded layout; the pads' gradients are 0)."""
+    u = info.unpadded
+    if u is not None:
+        grads = _attn_bwd(*(repack_rows(t, u, info) for t in (q, k, v, o)), lse, repack_rows(dout, u, info), u,
+                          softmax_scale)
+        return tuple(repack_rows(g, info, u) for g in grads)
+    return _attn_bwd(q, k, v, o, lse, dout, info, softmax_scale)
+
+
+def _attn_bwd(q, k, v, o, lse, dout, info, softmax_scale):
     plan = info.plan
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
         _need_cuda(t, name)

@@ -266,6 +266,7 @@ __global__ void __launch_bounds__(kFinalThreads) k_seg_offsets(int B, int32_t *_
   if (threadIdx.x == 0) {
     plan.counts[1] = base;
     plan.counts[2] = 0;
+    plan.counts[3] = 0;
   }
 }
 
@@ -308,7 +309,9 @@ __global__ void __launch_bounds__(256) k_scatter(int64_t S, int64_t P, const int
   const int r = plan.rep[g];
   const int po = plan.prompt_off[g];
   const int ro = plan.resp_off[b];
-  int pads = 0;
+  int pads = 0;       // (b, t) mapped to no packed row (unpad mode)
+  int kept_pads = 0;  // packed rows whose mask entry is 0 (padded mode with a mask)
+  const bool count_kept_pads = !unpad && mask;
   // prompt columns: kept-ness and positions come from the first member
   for_kept_columns(mask, esz, unpad, int64_t(r) * S, 0, P, [&](int64_t t, bool kept, int rank) {
     const int j = po + rank;
@@ -320,6 +323,7 @@ __global__ void __launch_bounds__(256) k_scatter(int64_t S, int64_t P, const int
       plan.seg_start[j] = po;
       dids[j] = ids[s];
       dpos[j] = pos[s];
+      if (count_kept_pads) kept_pads += !mask_at(mask, esz, s);
     }
   });
   for_kept_columns(mask, esz, unpad, int64_t(b) * S, P, S, [&](int64_t t, bool kept, int rank) {
@@ -332,11 +336,16 @@ __global__ void __launch_bounds__(256) k_scatter(int64_t S, int64_t P, const int
       plan.seg_start[j] = ro;
       dids[j] = ids[s];
       dpos[j] = pos[s];
+      if (count_kept_pads) kept_pads += !mask_at(mask, esz, s);
     }
   });
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) pads += __shfl_xor(pads, off, 64);
+  for (int off = 32; off > 0; off >>= 1) {
+    pads += __shfl_xor(pads, off, 64);
+    kept_pads += __shfl_xor(kept_pads, off, 64);
+  }
   if (__lane_id() == 0 && pads) atomicAdd(&plan.counts[2], pads);
+  if (__lane_id() == 0 && kept_pads) atomicAdd(&plan.counts[3], kept_pads);
 }
 
 // ----------------------------------------------------------------------------

@@ -128,6 +128,18 @@ def test_standard_mode_calls_reject_bad_arguments():
     assert lib.spd_repack_rows_bwd(ctypes.byref(p), 5, ctypes.byref(q), 0, A[12], 32, 1, A[13], None) == OK
 
 
+def test_varlen_calls_reject_bad_arguments():
+    ws = lib.spd_mask_varlen_workspace_bytes(10)
+    assert ws > 0 and lib.spd_mask_varlen_workspace_bytes(0) == 0
+    assert lib.spd_mask_to_varlen(A[10], 3, 10, 10, A[11], A[12], A[13], A[14], ws, None) == INVALID   # elem size
+    assert lib.spd_mask_to_varlen(A[10], 1, 0, 10, A[11], A[12], A[13], A[14], ws, None) == INVALID    # no rows
+    assert lib.spd_mask_to_varlen(None, 1, 10, 10, A[11], A[12], A[13], A[14], ws, None) == INVALID
+    assert lib.spd_mask_to_varlen(A[10], 1, 10, 10, A[11], A[12], A[13], A[14], ws - 1, None) == WS
+    assert lib.spd_mask_to_varlen(A[10], 8, 10, 2**28, A[11], A[12], A[13], A[14], ws, None) == UNSUPPORTED
+    p = _plan()
+    assert lib.spd_varlen_params(ctypes.byref(p), None, A[13], A[14], A[15], None) == INVALID
+
+
 def _desc(**kw):
     d = dict(num_q_heads=16, num_kv_heads=8, head_dim=128, dtype=1, softmax_scale=0.088)
     d.update(kw)

@@ -314,3 +314,48 @@ def test_full_visibility_probes(full):
         err = np.abs(on - target).max(axis=(1, 2))
         assert (err[sees] <= 2e-2).all(), f"rows that see key {js} missed it: {rows[sees][err[sees] > 2e-2][:10]}"
         assert (err[~sees] > 0.25).all(), f"rows that cannot see key {js} saw it: {rows[~sees][err[~sees] <= 0.25][:10]}"
+
+
+def test_padded_format_with_mask():
+    """Working with Packed/Unpacked Sequences, padded format: pads stay in the packed batch and take no part in
+    attention (output 0, zero gradients); checked against the oracle's masked definition, through the functional
+    calls, the autograd wrapper and the standard (full-batch) mode."""
+    import dataclasses
+    import shared_prompt_dedup_amd as spd
+    w = SMALL["bf16_gqa2_ragged_unpad"]
+    bt = make_batch(w, permute=True)
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    mask = bt.attention_mask.copy()
+    mask[groups[0], :4] = 0                        # left pads on group 0's prompt, right pads in responses
+    bt = dataclasses.replace(bt, attention_mask=mask)
+    _, _, oinfo = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
+                                                   attention_mask=mask, use_unpad=False)
+    valid = mask.reshape(-1)[oinfo["src"]] != 0
+    ids, pos, m = (torch.from_numpy(a).cuda() for a in (bt.input_ids, bt.position_ids, mask))
+    gg, gu = spd.find_prompt_groups(ids, bt.response_length)
+    _, _, ginfo = spd.create_deduplicated_batch(ids, pos, bt.response_length, gg, gu, attention_mask=m,
+                                                use_unpad=False)
+    say(f"[attn padded+mask] T={oinfo['T']} pads kept={int((~valid).sum())}")
+    assert ginfo["T"] == oinfo["T"] and ginfo["kept_pads"] == int((~valid).sum()) > 4
+    assert ginfo.unpadded is not None and ginfo.unpadded["T"] == int(valid.sum())
+    x, q, k, v, do = attn_inputs(w, oinfo["T"])
+    ro, _ = oracle.split_attention_forward(x.q, x.k, x.v, oinfo, valid=valid)
+    rgrads = oracle.split_attention_backward(x.q, x.k, x.v, x.do, oinfo, valid=valid)
+    o, lse = spd.split_attn_fwd(q, k, v, ginfo)
+    assert tuple(lse.shape) == (w.num_q_heads, ginfo.unpadded["T"])
+    grads = spd.split_attn_bwd(q, k, v, o, lse, do, ginfo)
+    compare("o", to_numpy(o), ro, "bf16")
+    for name, g, r in zip(("dq", "dk", "dv"), grads, rgrads):
+        compare(name, to_numpy(g), r, "bf16")
+    pads = torch.from_numpy(~valid).cuda()
+    assert not o[pads].any() and not any(g[pads].any() for g in grads)
+    # autograd wrapper and standard mode on the same batch
+    for label, fn in (("split", lambda a, b, c: spd.split_attention(a, b, c, ginfo)),
+                      ("standard", lambda a, b, c: spd.standard_attention(
+                          a, b, c, ginfo, spd.create_full_batch(ids, pos, bt.response_length, attention_mask=m)[2]))):
+        qg, kg, vg = (t.clone().requires_grad_() for t in (q, k, v))
+        out = fn(qg, kg, vg)
+        out.backward(do)
+        compare(f"{label} o", to_numpy(out.detach()), ro, "bf16")
+        for name, g, r in zip(("dq", "dk", "dv"), (qg.grad, kg.grad, vg.grad), rgrads):
+            compare(f"{label} {name}", to_numpy(g), r, "bf16")
