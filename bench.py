@@ -96,7 +96,7 @@ def cpu_baseline(w, bt, pairs_per_head, min_seconds=10.0):
         blas_threads = 1
     groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
     _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
-                                                  attention_mask=bt.attention_mask, use_unpad=w.use_unpad)
+                                                  attention_mask=bt.attention_mask, use_unpad=use_unpad)
     x = make_attn_inputs(w, info["T"])
     heads = 0
     dt = 0.0
@@ -123,9 +123,11 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name in workloads.WORKLOADS")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--profile-steps", type=int, default=5, help="steps timed per kernel with HIP events")
-    ap.add_argument("--mode", choices=("split", "standard"), default="split",
-                    help="split attention on the deduplicated batch (default), or the standard QKV mode: the "
-                         "same layer with attention run per sample on the full batch")
+    ap.add_argument("--mode", choices=("split", "standard", "padded_mask"), default="split",
+                    help="split attention on the deduplicated batch (default); the standard QKV mode: the same "
+                         "layer with attention run per sample on the full batch; or padded_mask: a batch with "
+                         "padding packed in the padded format with its attention mask (pads kept, no part in "
+                         "attention; default workload long_2x8_p32768_r256to1024_unpad)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -140,8 +142,9 @@ def main():
     import shared_prompt_dedup_amd as spd
     from workloads import WORKLOADS, make_attn_inputs, make_batch
 
-    name = args.workload or BENCH_WORKLOAD
+    name = args.workload or ("long_2x8_p32768_r256to1024_unpad" if args.mode == "padded_mask" else BENCH_WORKLOAD)
     w = WORKLOADS[name]
+    use_unpad = w.use_unpad and args.mode != "padded_mask"
     assert w.dtype == "bf16"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -155,9 +158,9 @@ def main():
     W = Hq * d
 
     groups, uniq = spd.group(ids, R, return_lists=False)
-    _, _, info = spd.pack(ids, pos, R, groups, uniq, attention_mask=mask, use_unpad=w.use_unpad)
+    _, _, info = spd.pack(ids, pos, R, groups, uniq, attention_mask=mask, use_unpad=use_unpad)
     T = info["T"]
-    pairs = attended_pairs(info)
+    pairs = attended_pairs(info.unpadded if info.unpadded is not None else info)
     x = make_attn_inputs(w, T)
     conv = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
     q, k, v = conv(x.q_bits), conv(x.k_bits), conv(x.v_bits)
@@ -168,7 +171,7 @@ def main():
 
     def step_split():
         g, u = spd.group(ids, R, return_lists=False)
-        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=w.use_unpad)
+        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=use_unpad)
         packed = spd.pack_rows(hidden, inf)
         o, lse = spd.split_attn_fwd(q, k, v, inf)
         out = spd.reconstruct(o.view(T, W), inf)
@@ -181,8 +184,8 @@ def main():
         # Standard QKV: Q, K, V reconstructed to the full batch (every sample its own prompt copy), attention
         # per sample there, output and gradients moved back to the deduplicated layout.
         g, u = spd.group(ids, R, return_lists=False)
-        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=w.use_unpad)
-        _, _, full = spd.create_full_batch(ids, pos, R, attention_mask=mask, use_unpad=w.use_unpad)
+        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=use_unpad)
+        _, _, full = spd.create_full_batch(ids, pos, R, attention_mask=mask, use_unpad=use_unpad)
         packed = spd.pack_rows(hidden, inf)
         qf, kf, vf = (spd.repack_rows(t, full, inf) for t in (q, k, v))
         of, lsef = spd.split_attn_fwd(qf, kf, vf, full)
@@ -195,10 +198,10 @@ def main():
         dhidden = spd.pack_rows_bwd(dq.view(T, W), inf)
         return packed, out, dhidden, dk, dv
 
-    step = step_split if args.mode == "split" else step_standard
+    step = step_standard if args.mode == "standard" else step_split
     kernel_pairs = pairs
     if args.mode == "standard":
-        _, _, full0 = spd.create_full_batch(ids, pos, R, attention_mask=mask, use_unpad=w.use_unpad)
+        _, _, full0 = spd.create_full_batch(ids, pos, R, attention_mask=mask, use_unpad=use_unpad)
         kernel_pairs = attended_pairs(full0)      # what the full-batch attention evaluates
         T_full = full0["T"]
         del full0
@@ -224,7 +227,11 @@ def main():
     prof = spd.profile_end()
     kern_ms = {kname: (tot / n if n else None) for kname, (n, tot) in prof.items()}
     row_bytes = W * 2
-    Ta = T if args.mode == "split" else T_full    # rows the attention kernels run on
+    Ta = {"split": T, "standard": None, "padded_mask": None}[args.mode]     # rows the attention kernels run on
+    if args.mode == "standard":
+        Ta = T_full
+    elif args.mode == "padded_mask":
+        Ta = info.unpadded["T"] if info.unpadded is not None else T
     kernel_work = {
         "fwd": ("mfma", 4 * d * Hq * kernel_pairs),
         "bwd_dkdv": ("mfma", 8 * d * Hq * kernel_pairs),      # S, dP recomputed; dV, dK
@@ -248,6 +255,27 @@ def main():
             ach = work / (ms * 1e-3) / 1e9
             kernels[kname] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    # Flash Attention Integration: the block-diagonal prompt-to-prompt mask of this batch -> cu_seqlens.
+    if args.mode == "split":
+        G = info["G"]
+        pl = info["prompt_len"][:G].to(torch.int64)
+        ptot = int(pl.sum().item())
+        if ptot > 0:
+            blk = torch.repeat_interleave(torch.arange(G, device=dev), pl)
+            ar = torch.arange(ptot, device=dev)
+            pmask = (blk[:, None] == blk[None, :]) & (ar[None, :] <= ar[:, None])
+            spd.attention_mask_to_flash_attn_params(pmask)
+            torch.cuda.synchronize()
+            spd.profile_begin()
+            for _ in range(5):
+                spd.attention_mask_to_flash_attn_params(pmask)
+            torch.cuda.synchronize()
+            n_mv, tot_mv = spd.profile_end()["mask_to_varlen"]
+            ms = tot_mv / n_mv
+            ach = ptot * ptot / (ms * 1e-3) / 1e9
+            kernels["mask_to_varlen"] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1),
+                                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+            del pmask, blk, ar
     # Practical HBM reference: a plain device-to-device copy of 1 GiB (read + write).
     src_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst_buf = torch.empty_like(src_buf)

@@ -348,7 +348,8 @@ enum {
   SPD_K_PACK_ROWS = 5,    /* row packing gather */
   SPD_K_RECONSTRUCT_BWD = 6,  /* backward of reconstruct: segment sum */
   SPD_K_PACK_ROWS_BWD = 7,    /* backward of pack_rows: scatter (and the zero fill) */
-  SPD_K_COUNT = 8
+  SPD_K_MASK_VARLEN = 8,      /* spd_mask_to_varlen: all four launches */
+  SPD_K_COUNT = 9
 };
 spd_status spd_profile_begin(void);
 spd_status spd_profile_end(int64_t *launches, double *total_ms);

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspd.so")
 
 SPD_OK = 0
 SPD_K_NAMES = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "reconstruct", "pack_rows", "reconstruct_bwd",
-               "pack_rows_bwd")
+               "pack_rows_bwd", "mask_to_varlen")
 SPD_F32 = 0
 SPD_BF16 = 1
 

@@ -227,6 +227,7 @@ extern "C" spd_status spd_mask_to_varlen(const void *mask, int32_t mask_elem_byt
   int32_t *last = reinterpret_cast<int32_t *>(ws + part);
   int32_t *owner = reinterpret_cast<int32_t *>(ws + 2 * part);
   const int Tq = int(total_q);
+  prof_start(SPD_K_MASK_VARLEN, st);
   const int64_t waves_grid = std::min<int64_t>((total_q + 3) / 4, int64_t(device_cu_count()) * 16);
   hipLaunchKernelGGL(k_row_extent, dim3(unsigned(std::max<int64_t>(1, waves_grid))), dim3(256), 0, st,
                      static_cast<const unsigned char *>(mask), total_q, int(total_kv * mask_elem_bytes),
@@ -239,6 +240,7 @@ extern "C" spd_status spd_mask_to_varlen(const void *mask, int32_t mask_elem_byt
   hipLaunchKernelGGL(k_mask_check, dim3((Tq + 255) / 256), dim3(256), 0, st, Tq, first, last, cu_seqlens_q,
                      cu_seqlens_k, stats);
   SPD_LAUNCH_CHECK();
+  prof_stop(SPD_K_MASK_VARLEN, st);
   return SPD_OK;
 }
 
