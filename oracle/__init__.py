@@ -25,14 +25,14 @@ mapped onto the packed rows.  Pins (tests/test_oracle_*.py) tie each function
 to something other than itself: the pages' worked examples, brute force,
 closed forms, a library attention routine, autograd and finite differences.
 """
-from .dedup import (find_prompt_groups, create_deduplicated_batch, reconstruct_sequences,
+from .dedup import (find_prompt_groups, find_shared_prefix, create_deduplicated_batch, reconstruct_sequences,
                     pack_rows, reconstruct_backward, pack_rows_backward, sample_rows, redundancy_counts,
                     attention_mask_to_flash_attn_params, varlen_params)
 from .attention import (split_attention_forward, split_attention_backward,
                         forward_rows, dq_rows, dkdv_rows, attended_pairs)
 
 __all__ = [
-    "find_prompt_groups", "create_deduplicated_batch", "reconstruct_sequences", "pack_rows",
+    "find_prompt_groups", "find_shared_prefix", "create_deduplicated_batch", "reconstruct_sequences", "pack_rows",
     "reconstruct_backward", "pack_rows_backward", "sample_rows", "redundancy_counts",
     "attention_mask_to_flash_attn_params", "varlen_params",
     "split_attention_forward", "split_attention_backward", "forward_rows", "dq_rows",

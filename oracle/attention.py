@@ -13,14 +13,15 @@ softmax attention separately on every sample's own ``[prompt][response]``
 sequence (gathered from the packed rows), in fp64, and maps the results
 back onto the packed rows:
 
-* forward -- response rows take their sample's output; prompt rows take the
-  output of the group's first member, and every other member's prompt
-  output is asserted equal to it (the deduplication invariant);
+* forward -- each packed row takes the output of the sample it was packed
+  from (response rows: their sample; prompt rows: the group's first member;
+  a shared prefix: the first sample), and every other sample's output for
+  that row is asserted equal to it (the deduplication invariant);
 * backward -- the gradient w.r.t. the packed tensors of
   ``O_packed = assemble(attention of every sample)``: each sample's ``dO``
-  is the packed ``dO`` on its response rows and, on its prompt rows, the
-  packed ``dO`` for the group's first member and 0 for the others (prompt
-  outputs were taken from the first member only); per-sample textbook
+  is the packed ``dO`` on the rows packed from it and 0 on the shared rows
+  packed from another sample (their outputs were taken from that sample
+  only); per-sample textbook
   gradients are scatter-added onto the packed rows, so prompt keys and
   values collect the gradient of every response that reads them.
 
@@ -89,20 +90,23 @@ def _prep(q, k, v, scale):
 
 
 def _sample_seq(info, b, valid):
-    """Packed rows of sample ``b``'s sequence and how many of them are prompt rows.
+    """Packed rows of sample ``b``'s sequence (ascending).
 
     With ``valid`` (bool per packed row; Working with Packed/Unpacked
     Sequences, padded format with an attention mask) the pads are left out of
     the sequence: they are no sample's keys or queries, so their outputs and
     gradients stay 0.
     """
-    g = info["group_of"][b]
-    pl = int(info["prompt_len"][g])
     idx = sample_rows(info, b)
     if valid is None:
-        return idx, pl
-    keep = np.asarray(valid, dtype=bool)[idx]
-    return idx[keep], int(keep[:pl].sum())
+        return idx
+    return idx[np.asarray(valid, dtype=bool)[idx]]
+
+
+def _owner(info):
+    """The sample each packed row was packed from: its output is that
+    sample's, and only that sample carries its ``dO`` in the backward."""
+    return np.asarray(info["src"], dtype=np.int64) // int(info["S"])
 
 
 def _members_rep_first(info, g):
@@ -121,11 +125,14 @@ def split_attention_forward(q, k, v, info, scale=None, heads=None, valid=None):
     heads = range(Hq) if heads is None else heads
     o = np.zeros((T, Hq, d))
     lse = np.zeros((Hq, T))
+    owner = _owner(info)
     for g in range(info["G"]):
-        rep = int(info["rep"][g])
+        # a group's first member first: it owns the group's prompt rows (and
+        # the first group's first member owns a shared prefix)
         for b in _members_rep_first(info, g):
-            idx, pl = _sample_seq(info, b, valid)
+            idx = _sample_seq(info, b, valid)
             L = len(idx)
+            mine = owner[idx] == b
             for h in heads:
                 j = _kv_head(h, Hq, Hkv)
                 Qs, Ks, Vs = q[idx, h], k[idx, j], v[idx, j]
@@ -134,15 +141,11 @@ def split_attention_forward(q, k, v, info, scale=None, heads=None, valid=None):
                 for i0 in range(0, L, _BLOCK):
                     i1 = min(L, i0 + _BLOCK)
                     _, Ob[i0:i1], Lb[i0:i1], _ = _causal_block(Qs, Ks, Vs, i0, i1, scale)
-                o[idx[pl:], h] = Ob[pl:]
-                lse[h, idx[pl:]] = Lb[pl:]
-                if b == rep:
-                    o[idx[:pl], h] = Ob[:pl]
-                    lse[h, idx[:pl]] = Lb[:pl]
-                else:
-                    # every copy of a prompt must produce the same prompt output
-                    err = np.max(np.abs(o[idx[:pl], h] - Ob[:pl]), initial=0.0)
-                    assert err <= 1e-12, f"prompt copies disagree by {err}"
+                o[idx[mine], h] = Ob[mine]
+                lse[h, idx[mine]] = Lb[mine]
+                # every copy of a shared row must produce the same output
+                err = np.max(np.abs(o[idx[~mine], h] - Ob[~mine]), initial=0.0)
+                assert err <= 1e-12, f"copies of a shared row disagree by {err}"
     return o, lse
 
 
@@ -161,17 +164,16 @@ def split_attention_backward(q, k, v, dout, info, scale=None, heads=None, valid=
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    owner = _owner(info)
     for g in range(info["G"]):
-        rep = int(info["rep"][g])
         for b in _members_rep_first(info, g):
-            idx, pl = _sample_seq(info, b, valid)
+            idx = _sample_seq(info, b, valid)
             L = len(idx)
             for h in heads:
                 j = _kv_head(h, Hq, Hkv)
                 Qs, Ks, Vs = q[idx, h], k[idx, j], v[idx, j]
                 dOs = dout[idx, h].copy()
-                if b != rep:
-                    dOs[:pl] = 0.0
+                dOs[owner[idx] != b] = 0.0
                 dQb = np.zeros((L, d))
                 dKb = np.zeros((L, d))
                 dVb = np.zeros((L, d))
@@ -194,14 +196,10 @@ def split_attention_backward(q, k, v, dout, info, scale=None, heads=None, valid=
 # ---------------------------------------------------------------------------
 
 def _locate(info, j):
-    """(sample, position in that sample's sequence, is_prompt) of packed row ``j``."""
-    S, P = info["S"], info["P"]
-    src = int(info["src"][j])
-    b0, t = divmod(src, S)
-    g = int(info["group_of"][b0])
-    if t < P:
-        return int(info["rep"][g]), j - int(info["prompt_off"][g]), True
-    return b0, int(info["prompt_len"][g]) + (j - int(info["resp_off"][b0])), False
+    """(owning sample, position of packed row ``j`` in that sample's sequence)."""
+    b = int(info["src"][j]) // int(info["S"])
+    idx = sample_rows(info, b)
+    return b, int(np.searchsorted(idx, j))
 
 
 def forward_rows(q, k, v, info, rows, heads, scale=None):
@@ -213,7 +211,7 @@ def forward_rows(q, k, v, info, rows, heads, scale=None):
     o = np.zeros((len(rows), len(heads), d))
     lse = np.zeros((len(rows), len(heads)))
     for a, j in enumerate(rows):
-        b, i, _ = _locate(info, int(j))
+        b, i = _locate(info, int(j))
         idx = sample_rows(info, b)
         for c, h in enumerate(heads):
             kv = _kv_head(h, Hq, Hkv)
@@ -226,19 +224,21 @@ def forward_rows(q, k, v, info, rows, heads, scale=None):
 def dq_rows(q, k, v, dout, info, rows, heads, scale=None):
     """``dq`` for the listed packed rows and query heads (``[len(rows), len(heads), d]``).
 
-    Only the owning sample has a non-zero ``dO`` on a row (prompt rows: the
-    group's first member), so the row's gradient is that sample's.
+    Only the owning sample has a non-zero ``dO`` on a row (shared rows: the
+    sample they were packed from), so the row's gradient is that sample's.
     """
     q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
     dout = np.asarray(dout, dtype=np.float64)
     out = np.zeros((len(rows), len(heads), d))
     for a, j in enumerate(rows):
-        b, i, _ = _locate(info, int(j))
+        b, i = _locate(info, int(j))
         idx = sample_rows(info, b)
+        owner = _owner(info)[idx]
         for c, h in enumerate(heads):
             kv = _kv_head(h, Hq, Hkv)
             Ks = k[idx, kv]
-            _, _, _, dS = _causal_block(q[idx, h], Ks, v[idx, kv], i, i + 1, scale, dout[idx, h])
+            _, _, _, dS = _causal_block(q[idx, h], Ks, v[idx, kv], i, i + 1, scale,
+                                        np.where((owner == b)[:, None], dout[idx, h], 0.0))
             out[a, c] = scale * (dS @ Ks[:i + 1])[0]
     return out
 
@@ -255,24 +255,24 @@ def dkdv_rows(q, k, v, dout, info, keys, kv_heads, scale=None):
     ratio = Hq // Hkv
     dk = np.zeros((len(keys), len(kv_heads), d))
     dv = np.zeros((len(keys), len(kv_heads), d))
+    owner_all = _owner(info)
     for a, kr in enumerate(keys):
         kr = int(kr)
-        b0, kpos, is_prompt = _locate(info, kr)
-        g = int(info["group_of"][b0])
-        pl = int(info["prompt_len"][g])
-        rep = int(info["rep"][g])
-        samples = _members_rep_first(info, g) if is_prompt else [b0]
-        for b in samples:
+        for b in range(info["B"]):
             idx = sample_rows(info, b)
+            kpos = int(np.searchsorted(idx, kr))
+            if kpos >= len(idx) or idx[kpos] != kr:
+                continue                       # the key is not in this sample's sequence
+            own = owner_all[idx] == b
+            later = np.flatnonzero(own[kpos:])
+            if not len(later):
+                continue                       # no query of this sample that sees the key carries dO
+            first = kpos + int(later[0])
             L = len(idx)
-            # query positions that see this key and carry a non-zero dO
-            first = kpos if (b == rep or not is_prompt) else pl
             for c, j in enumerate(kv_heads):
                 for h in range(j * ratio, (j + 1) * ratio):
                     Qs, Ks, Vs = q[idx, h], k[idx, j], v[idx, j]
-                    dOs = dout[idx, h].copy()
-                    if b != rep:
-                        dOs[:pl] = 0.0
+                    dOs = np.where(own[:, None], dout[idx, h], 0.0)
                     for i0 in range(first, L, _BLOCK):
                         i1 = min(L, i0 + _BLOCK)
                         p, _, _, dS = _causal_block(Qs, Ks, Vs, i0, i1, scale, dOs)
@@ -285,17 +285,20 @@ def attended_pairs(info):
     """Number of (query, key) pairs split attention evaluates on the packed batch.
 
     Prompt ``g``: ``Pl (Pl + 1) / 2`` causal pairs once; response ``b``:
-    ``Rl * Pl`` prompt keys plus ``Rl (Rl + 1) / 2`` causal own pairs.
+    ``Rl * Pl`` prompt keys plus ``Rl (Rl + 1) / 2`` causal own pairs.  With
+    a shared prefix of ``Lp`` rows: ``Lp (Lp + 1) / 2`` once, and every
+    prompt and response row also sees the ``Lp`` prefix keys.
     Also returns the non-deduplicated count, ``sum_b L_b (L_b + 1) / 2``.
     """
-    dedup = 0
+    lp = int(info.get("prefix_len", 0))
+    dedup = lp * (lp + 1) // 2
     plain = 0
     for g in range(info["G"]):
         pl = int(info["prompt_len"][g])
-        dedup += pl * (pl + 1) // 2
+        dedup += pl * lp + pl * (pl + 1) // 2
         for b in info["groups"][g]:
             rl = int(info["resp_len"][b])
-            dedup += rl * pl + rl * (rl + 1) // 2
-            L = pl + rl
+            dedup += rl * (lp + pl) + rl * (rl + 1) // 2
+            L = lp + pl + rl
             plain += L * (L + 1) // 2
     return dedup, plain

@@ -53,8 +53,30 @@ def find_prompt_groups(input_ids: np.ndarray, response_length: int):
     return groups, unique_prompts
 
 
+def find_shared_prefix(input_ids, response_length, prompt_groups):
+    """Key Limitations & Future Work -- prefix caching for partially
+    overlapping prompts (the pages name it as a future direction; this is
+    the plainest form of it).
+
+    The number of leading prompt columns on which the first members of all
+    groups agree: the batch's shared prefix.  0 with fewer than two groups
+    (a single group already shares its whole prompt).
+    """
+    ids = np.asarray(input_ids)
+    P = ids.shape[1] - int(response_length)
+    if len(prompt_groups) < 2:
+        return 0
+    ref = ids[prompt_groups[0][0], :P]
+    L = P
+    for members in prompt_groups[1:]:
+        diff = np.flatnonzero(ids[members[0], :P] != ref)
+        if len(diff):
+            L = min(L, int(diff[0]))
+    return L
+
+
 def create_deduplicated_batch(input_ids, position_ids, response_length, prompt_groups,
-                              unique_prompts, attention_mask=None, use_unpad=False):
+                              unique_prompts, attention_mask=None, use_unpad=False, prefix_len=0):
     """How Prompt Deduplication Works -- Creating Deduplicated Batch; Working with
     Packed/Unpacked Sequences.
 
@@ -69,6 +91,13 @@ def create_deduplicated_batch(input_ids, position_ids, response_length, prompt_g
     kept, in order); and ``src[T]`` (packed row -> ``b*S + t``), ``dst[B*S]``
     ((b, t) -> packed row, or -1), ``seg_start[T]`` (first packed row of the
     segment each packed row lies in).
+
+    With ``prefix_len = L0 > 0`` (a shared prefix, see ``find_shared_prefix``)
+    the first ``L0`` prompt columns are packed once, from the first sample,
+    ahead of everything: ``[prefix][suffix_1][responses of 1][suffix_2]...``,
+    and a group's "prompt" segment is its suffix (columns ``L0..P-1``).
+    ``info`` then also holds ``L0``, ``prefix_len`` (packed rows) and
+    ``prefix_cols``.
     """
     ids = np.asarray(input_ids)
     pos = np.asarray(position_ids)
@@ -92,10 +121,17 @@ def create_deduplicated_batch(input_ids, position_ids, response_length, prompt_g
     resp_len = np.zeros(B, np.int64)
     prompt_cols = [None] * B
     resp_cols = [None] * B
+    L0 = int(prefix_len)
+    if not 0 <= L0 <= P:
+        raise ValueError("prefix_len must lie in [0, P]")
+    r0 = prompt_groups[0][0] if len(prompt_groups) else 0
+    prefix_cols = np.flatnonzero(keep[r0, :L0]) if L0 else np.zeros(0, np.int64)
+    src.extend(int(r0 * S + t) for t in prefix_cols)
+    seg_start.extend([0] * len(prefix_cols))
     for g, members in enumerate(prompt_groups):
         r = members[0]
         rep[g] = r
-        cols = np.flatnonzero(keep[r, :P])
+        cols = L0 + np.flatnonzero(keep[r, L0:P])
         prompt_off[g] = len(src)
         prompt_len[g] = len(cols)
         src.extend(int(r * S + t) for t in cols)
@@ -114,6 +150,7 @@ def create_deduplicated_batch(input_ids, position_ids, response_length, prompt_g
     dst = np.full(B * S, -1, np.int64)
     for b in range(B):
         g = group_of[b]
+        dst[b * S + prefix_cols] = np.arange(len(prefix_cols))
         dst[b * S + prompt_cols[b]] = prompt_off[g] + np.arange(prompt_len[g])
         dst[b * S + resp_cols[b]] = resp_off[b] + np.arange(resp_len[b])
     flat_ids = ids.reshape(-1)
@@ -124,7 +161,8 @@ def create_deduplicated_batch(input_ids, position_ids, response_length, prompt_g
                 rep=rep, group_of=group_of, prompt_off=prompt_off, prompt_len=prompt_len,
                 resp_off=resp_off, resp_len=resp_len, prompt_cols=prompt_cols,
                 resp_cols=resp_cols, src=src_a, dst=dst,
-                seg_start=np.asarray(seg_start, dtype=np.int64))
+                seg_start=np.asarray(seg_start, dtype=np.int64),
+                L0=L0, prefix_len=len(prefix_cols), prefix_cols=prefix_cols)
     return dedup_ids, dedup_pos, info
 
 
@@ -140,8 +178,11 @@ def reconstruct_sequences(dedup_hidden, info):
         x = x[0]
     B, S = info["B"], info["S"]
     out = np.zeros((B, S) + x.shape[1:], dtype=x.dtype)
+    lp = info.get("prefix_len", 0)
     for b in range(B):
         g = info["group_of"][b]
+        if lp:
+            out[b, info["prefix_cols"]] = x[:lp]
         po, pl = info["prompt_off"][g], info["prompt_len"][g]
         out[b, info["prompt_cols"][b]] = x[po:po + pl]
         ro, rl = info["resp_off"][b], info["resp_len"][b]
@@ -174,8 +215,11 @@ def reconstruct_backward(dout, info):
     """
     x = np.asarray(dout, dtype=np.float64)
     out = np.zeros((info["T"],) + x.shape[2:], dtype=np.float64)
+    lp = info.get("prefix_len", 0)
     for b in range(info["B"]):
         g = info["group_of"][b]
+        if lp:
+            out[:lp] += x[b, info["prefix_cols"]]
         po, pl = info["prompt_off"][g], info["prompt_len"][g]
         out[po:po + pl] += x[b, info["prompt_cols"][b]]
         ro, rl = info["resp_off"][b], info["resp_len"][b]
@@ -270,7 +314,8 @@ def varlen_params(info):
 
 
 def sample_rows(info, b):
-    """Packed rows of sample ``b``'s own sequence: its group's prompt, then its response.
+    """Packed rows of sample ``b``'s own sequence: the shared prefix (if any), its group's
+    prompt, then its response (ascending in the packed layout).
 
     This is the non-deduplicated ``[Prompt][Response]`` sample expressed as
     packed row indices (Phase 1 diagram: every sample is its prompt followed
@@ -279,7 +324,8 @@ def sample_rows(info, b):
     g = info["group_of"][b]
     po, pl = info["prompt_off"][g], info["prompt_len"][g]
     ro, rl = info["resp_off"][b], info["resp_len"][b]
-    return np.concatenate([np.arange(po, po + pl), np.arange(ro, ro + rl)]).astype(np.int64)
+    lp = info.get("prefix_len", 0)
+    return np.concatenate([np.arange(lp), np.arange(po, po + pl), np.arange(ro, ro + rl)]).astype(np.int64)
 
 
 def redundancy_counts(info):
@@ -289,7 +335,7 @@ def redundancy_counts(info):
     non-deduplicated batch), ``unique`` counts the packed tokens, and
     ``redundancy = 1 - unique / total``.
     """
-    total = int(sum(info["prompt_len"][info["group_of"][b]] + info["resp_len"][b]
+    total = int(sum(info.get("prefix_len", 0) + info["prompt_len"][info["group_of"][b]] + info["resp_len"][b]
                     for b in range(info["B"])))
     unique = int(info["T"])
     return total, unique, (1.0 - unique / total) if total else 0.0

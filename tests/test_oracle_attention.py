@@ -383,3 +383,88 @@ def test_planted_pad_key_leak_is_caught():
     wrong, _ = oracle.split_attention_forward(x.q, x.k, x.v, info)
     ref = _sdpa_packed_masked(*(torch.from_numpy(a.astype(np.float64)) for a in (x.q, x.k, x.v)), info, scale, valid)
     assert np.abs(wrong[valid] - ref.numpy()[valid]).max() > 1e-3
+
+
+# ---------------------------------------------------------------- shared prefix (prefix caching)
+
+def _prefix_setup(prefix=True, seed=91):
+    import importlib
+    tod = importlib.import_module("test_oracle_dedup")
+    ids, pos, mask, R = tod._prefix_batch(G=3, n=2, L=13, P=24, R=9, seed=seed, unpad=True)
+    groups, uniq = oracle.find_prompt_groups(ids, R)
+    L0 = oracle.find_shared_prefix(ids, R, groups) if prefix else 0
+    _, _, info = oracle.create_deduplicated_batch(ids, pos, R, groups, uniq, attention_mask=mask, use_unpad=True,
+                                                  prefix_len=L0)
+    return ids, mask, info
+
+
+def _qkv(T, seed=5, Hq=4, Hkv=2, d=16):
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal(s) * 0.7 for s in ((T, Hq, d), (T, Hkv, d), (T, Hkv, d), (T, Hq, d))]
+
+
+def _sdpa_owner(q, k, v, info):
+    """Per-sample torch SDPA over each sample's rows; each packed row from the sample it was packed from."""
+    T, Hq, d = q.shape
+    ratio = Hq // k.shape[1]
+    owner = np.asarray(info["src"]) // info["S"]
+    rows = [None] * T
+    for b in range(info["B"]):
+        idx = oracle.sample_rows(info, b)
+        ti = torch.as_tensor(idx)
+        Q = q[ti].transpose(0, 1)
+        K = k[ti].repeat_interleave(ratio, dim=1).transpose(0, 1)
+        V = v[ti].repeat_interleave(ratio, dim=1).transpose(0, 1)
+        ob = F.scaled_dot_product_attention(Q, K, V, is_causal=True).transpose(0, 1)
+        for i, j in enumerate(idx.tolist()):
+            if owner[j] == b:
+                rows[j] = ob[i]
+    return torch.stack(rows)
+
+
+def test_prefix_forward_backward_match_library():
+    ids, mask, info = _prefix_setup()
+    assert info["prefix_len"] == 13
+    q, k, v, do = _qkv(info["T"])
+    o, _ = oracle.split_attention_forward(q, k, v, info)
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_() for a in (q, k, v))
+    ref = _sdpa_owner(tq, tk, tv, info)
+    np.testing.assert_allclose(o, ref.detach().numpy(), rtol=0, atol=1e-12)
+    (ref * torch.from_numpy(do)).sum().backward()
+    for got, want in zip(oracle.split_attention_backward(q, k, v, do, info), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=0, atol=1e-11)
+
+
+def test_prefix_sharing_equals_exact_dedup_per_cell():
+    """Packing the shared prefix once changes the layout, not the function: per (sample, column) outputs
+    agree with the layout without it; a prefix key's gradient is the sum of the groups' copies."""
+    ids, mask, pinfo = _prefix_setup(prefix=True)
+    _, _, ninfo = _prefix_setup(prefix=False)
+    B, S = ids.shape
+    rng = np.random.default_rng(8)
+    cells = {n: rng.standard_normal((B, S, 4, 16)) * 0.7 for n in ("q", "do")}
+    kvc = {n: rng.standard_normal((B, S, 2, 16)) * 0.7 for n in ("k", "v")}
+    # the same per-cell inputs (identical copies across the cells a packed row stands for)
+    L0, P = pinfo["L0"], pinfo["P"]
+    for a in list(cells.values()) + list(kvc.values()):
+        a[:, :L0] = a[0, :L0]
+        for m in pinfo["groups"]:
+            a[m, L0:P] = a[m[0], L0:P]
+    cells["do"][1:, :L0] = 0.0          # prefix outputs used from sample 0 only, in both layouts
+    for m in ninfo["groups"]:
+        cells["do"][m[1:], :P] = 0.0
+    def run(info):
+        pk = {n: oracle.pack_rows(a, info) for n, a in {**cells, **kvc}.items()}
+        o, _ = oracle.split_attention_forward(pk["q"], pk["k"], pk["v"], info)
+        g = oracle.split_attention_backward(pk["q"], pk["k"], pk["v"], pk["do"], info)
+        return o, g
+    (op, gp), (on, gn) = run(pinfo), run(ninfo)
+    keep = mask != 0
+    flat = lambda a: a.reshape(a.shape[0], -1)
+    np.testing.assert_allclose(oracle.reconstruct_sequences(flat(op), pinfo)[keep],
+                               oracle.reconstruct_sequences(flat(on), ninfo)[keep], rtol=0, atol=1e-12)
+    # gradients: a packed row of the prefix layout collects the rows of the other layout it stands for
+    # (spread each to its source cell, then sum the cells each prefix-layout row stands for)
+    for a, b in zip(gp, gn):
+        want = oracle.reconstruct_backward(oracle.pack_rows_backward(flat(b), ninfo), pinfo)
+        np.testing.assert_allclose(flat(a), want, rtol=0, atol=1e-11)

@@ -414,3 +414,79 @@ def test_mask_to_flash_params_reports_non_block_masks():
     assert oracle.attention_mask_to_flash_attn_params(m)["mismatched_rows"] >= 1
     p = oracle.attention_mask_to_flash_attn_params(np.zeros((3, 5), bool))
     assert p["num_seqs"] == 0 and p["cu_seqlens_q"].tolist() == [0]
+
+
+# ---------------------------------------------------------------- shared prefix (prefix caching)
+
+def _prefix_batch(G=3, n=2, L=11, P=20, R=6, seed=61, vocab=9, unpad=False):
+    """G distinct prompts sharing their first L columns (and differing at column L), n responses each."""
+    rng = np.random.default_rng(seed)
+    B, S = G * n, P + R
+    ids = rng.integers(1, vocab, size=(B, S))
+    common = rng.integers(1, vocab, size=L)
+    tails = []
+    for g in range(G):
+        t = rng.integers(1, vocab, size=P - L)
+        if L < P:
+            t[0] = (g % (vocab - 1)) + 1          # column L differs between groups
+        tails.append(t)
+    for b in range(B):
+        ids[b, :L] = common
+        ids[b, L:P] = tails[b // n]
+    pos = np.tile(np.arange(S), (B, 1))
+    mask = np.ones((B, S), np.int64)
+    if unpad:
+        for b in range(B):
+            mask[b, P + int(rng.integers(0, R + 1)):] = 0
+    return ids, pos, mask, R
+
+
+@pytest.mark.parametrize("L", [0, 1, 7, 19, 20])
+def test_find_shared_prefix_planted(L):
+    ids, pos, mask, R = _prefix_batch(L=L)
+    groups, _ = oracle.find_prompt_groups(ids, R)
+    got = oracle.find_shared_prefix(ids, R, groups)
+    P = ids.shape[1] - R
+    # brute force over all pairs of samples
+    def lcp(a, b):
+        k = 0
+        while k < P and ids[a, k] == ids[b, k]:
+            k += 1
+        return k
+    brute = min(lcp(a, b) for a in range(len(ids)) for b in range(len(ids))) if len(groups) > 1 else 0
+    assert got == brute
+    if L < P:
+        assert got == L
+
+
+@pytest.mark.parametrize("unpad", [False, True])
+def test_prefix_layout_and_round_trip(unpad):
+    ids, pos, mask, R = _prefix_batch(unpad=unpad)
+    groups, uniq = oracle.find_prompt_groups(ids, R)
+    L0 = oracle.find_shared_prefix(ids, R, groups)
+    dids, dpos, info = oracle.create_deduplicated_batch(ids, pos, R, groups, uniq, attention_mask=mask,
+                                                        use_unpad=unpad, prefix_len=L0)
+    P = ids.shape[1] - R
+    keep = mask != 0
+    # [prefix once][suffix of g][responses of g] ...
+    expect = list(ids[0, :L0])
+    for m in groups:
+        expect += list(ids[m[0], L0:P])
+        for b in m:
+            expect += list(ids[b, P:][keep[b, P:]])
+    np.testing.assert_array_equal(np.asarray(dids).ravel(), expect)
+    assert info["prefix_len"] == L0 and info["T"] == L0 + sum(P - L0 for _ in groups) + keep[:, P:].sum()
+    X = np.random.default_rng(3).standard_normal((ids.shape[0], ids.shape[1], 4))
+    X[:, :L0] = X[0, :L0]
+    for m in groups:
+        X[m, :P] = X[m[0], :P]
+    Y = oracle.reconstruct_sequences(oracle.pack_rows(X, info), info)
+    np.testing.assert_array_equal(Y[keep], X[keep])
+    # backward of reconstruct: a prefix row collects every sample
+    g = oracle.reconstruct_backward(np.ones(ids.shape), info)
+    assert (g[:L0] == ids.shape[0]).all()
+    x = np.random.default_rng(4).standard_normal((info["T"], 3))
+    y = np.random.default_rng(5).standard_normal(ids.shape + (3,))
+    lhs = np.sum(oracle.reconstruct_sequences(x, info) * y)
+    rhs = np.sum(x * oracle.reconstruct_backward(y, info))
+    assert abs(lhs - rhs) <= 1e-12 * np.abs(y).sum() * np.abs(x).max()
