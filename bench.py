@@ -72,14 +72,16 @@ def measured_traffic(kernel, workload):
 
 
 def attended_pairs(info):
-    """(query, key) pairs split attention evaluates, from the plan's segment lengths."""
+    """(query, key) pairs split attention evaluates, from the plan's segment lengths (a shared prefix of Lp rows:
+    Lp (Lp + 1) / 2 once, and every later row also sees its Lp keys)."""
     G = info["G"]
+    lp = int(info.get("prefix_len", 0))
     pl = info["prompt_len"][:G].cpu().tolist()
     rl = info["resp_len"].cpu().tolist()
     gof = info["group_of"].cpu().tolist()
-    pairs = sum(p * (p + 1) // 2 for p in pl)
+    pairs = lp * (lp + 1) // 2 + sum(p * lp + p * (p + 1) // 2 for p in pl)
     for b, r in enumerate(rl):
-        pairs += r * pl[gof[b]] + r * (r + 1) // 2
+        pairs += r * (lp + pl[gof[b]]) + r * (r + 1) // 2
     return pairs
 
 
@@ -123,6 +125,9 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name in workloads.WORKLOADS")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--profile-steps", type=int, default=5, help="steps timed per kernel with HIP events")
+    ap.add_argument("--share-prefix", action="store_true",
+                    help="also pack the prompts' common prefix once (prefix caching); try it with --workload "
+                         "prefix_4x8_s4096_p5120_r512")
     ap.add_argument("--mode", choices=("split", "standard", "padded_mask"), default="split",
                     help="split attention on the deduplicated batch (default); the standard QKV mode: the same "
                          "layer with attention run per sample on the full batch; or padded_mask: a batch with "
@@ -158,7 +163,8 @@ def main():
     W = Hq * d
 
     groups, uniq = spd.group(ids, R, return_lists=False)
-    _, _, info = spd.pack(ids, pos, R, groups, uniq, attention_mask=mask, use_unpad=use_unpad)
+    _, _, info = spd.pack(ids, pos, R, groups, uniq, attention_mask=mask, use_unpad=use_unpad,
+                          share_prefix=args.share_prefix)
     T = info["T"]
     pairs = attended_pairs(info.unpadded if info.unpadded is not None else info)
     x = make_attn_inputs(w, T)
@@ -171,7 +177,8 @@ def main():
 
     def step_split():
         g, u = spd.group(ids, R, return_lists=False)
-        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=use_unpad)
+        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=use_unpad,
+                             share_prefix=args.share_prefix)
         packed = spd.pack_rows(hidden, inf)
         o, lse = spd.split_attn_fwd(q, k, v, inf)
         out = spd.reconstruct(o.view(T, W), inf)
@@ -184,7 +191,8 @@ def main():
         # Standard QKV: Q, K, V reconstructed to the full batch (every sample its own prompt copy), attention
         # per sample there, output and gradients moved back to the deduplicated layout.
         g, u = spd.group(ids, R, return_lists=False)
-        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=use_unpad)
+        _, _, inf = spd.pack(ids, pos, R, g, u, attention_mask=mask, use_unpad=use_unpad,
+                             share_prefix=args.share_prefix)
         _, _, full = spd.create_full_batch(ids, pos, R, attention_mask=mask, use_unpad=use_unpad)
         packed = spd.pack_rows(hidden, inf)
         qf, kf, vf = (spd.repack_rows(t, full, inf) for t in (q, k, v))
@@ -310,7 +318,7 @@ def main():
         "config": {"workload": name, "batch": B, "unique_prompts": w.num_prompts, "prompt_len": w.prompt_len,
                    "response_len": w.response_len, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "packed_tokens": T, "attended_pairs": pairs, "parallelism": "single GPU",
-                   "attention": args.mode},
+                   "attention": args.mode, "shared_prefix_rows": int(info.get("prefix_len", 0))},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "attention_kernels_tflops": round((fwd_flops + bwd_flops) / (attn_ms * 1e-3) / 1e12, 2),
         "roofline": roof,

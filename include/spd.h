@@ -93,9 +93,11 @@ typedef struct spd_plan {
   int32_t *src;         /* [B * S] capacity; packed row j -> b * S + t (first T used) */
   int32_t *dst;         /* [B * S] (b, t) -> packed row, or -1 if no packed token maps */
   int32_t *seg_start;   /* [B * S] capacity; first packed row of j's segment */
-  int32_t *counts;      /* [4]     counts[0] = G, counts[1] = T, counts[2] = batch cells mapped to
+  int32_t *counts;      /* [8]     counts[0] = G, counts[1] = T, counts[2] = batch cells mapped to
                                      no packed row (unpad mode), counts[3] = packed rows whose
-                                     attention-mask entry is 0 (padded mode with a mask) */
+                                     attention-mask entry is 0 (padded mode with a mask),
+                                     counts[4] = L0, prompt columns of a shared prefix (0: none),
+                                     counts[5] = packed rows of that prefix, [6..7] reserved */
 } spd_plan;
 
 /* ---------------------------------------------------------------- grouping */
@@ -200,6 +202,20 @@ spd_status spd_reconstruct_bwd(const spd_plan *plan, int64_t T, const void *dout
  */
 spd_status spd_pack_rows_bwd(const spd_plan *plan, int64_t T, const void *dpacked, int64_t row_bytes,
                              void *drows, void *stream);
+
+/*
+ * Shared prompt prefix ("Key Limitations & Future Work": prefix caching for
+ * partially overlapping prompts).  After spd_group: counts[4] = L0, the number
+ * of leading prompt columns on which the first members of all groups agree
+ * (0 with fewer than two groups).  spd_pack then packs those columns once,
+ * from the first sample, ahead of every group -- [prefix][prompt 1][responses
+ * of 1][prompt 2]... with prompt g now its columns L0..P-1 -- and every call
+ * that takes the plan (attention, reconstruct, row moves) treats the prefix
+ * rows as part of every sample's sequence.  Without this call spd_group
+ * leaves counts[4] = 0 (no prefix level).
+ */
+spd_status spd_share_prefix(const int64_t *input_ids, int64_t B, int64_t S, int64_t response_length,
+                            const spd_plan *plan, void *stream);
 
 /*
  * The plan of the non-deduplicated batch: every sample is its own group

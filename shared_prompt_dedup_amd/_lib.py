@@ -50,6 +50,8 @@ _SIG = {
     "spd_reconstruct_bwd": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, _P, ctypes.c_int64,
                                            ctypes.c_int32, _P, _P]),
     "spd_pack_rows_bwd": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, _P, ctypes.c_int64, _P, _P]),
+    "spd_share_prefix": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(SpdPlan),
+                                        _P]),
     "spd_group_singletons": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(SpdPlan),
                                             _P]),
     "spd_repack_rows": (ctypes.c_int, [ctypes.POINTER(SpdPlan), ctypes.c_int64, ctypes.POINTER(SpdPlan),

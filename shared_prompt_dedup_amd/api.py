@@ -62,11 +62,13 @@ class Plan:
         self.src = torch.empty(n, **i32)
         self.dst = torch.empty(n, **i32)
         self.seg_start = torch.empty(n, **i32)
-        self.counts = torch.zeros(4, **i32)
+        self.counts = torch.zeros(8, **i32)
         self.G: Optional[int] = None
         self.T: Optional[int] = None
         self.use_unpad = False
         self.kept_pads = 0
+        self.L0 = 0
+        self.prefix_len = 0
         self._c = SpdPlan(self.B, self.S, self.P, *[t.data_ptr() for t in
                                                     (getattr(self, f) for f in _PLAN_FIELDS)])
 
@@ -78,6 +80,7 @@ class Plan:
         c = self.counts.cpu().tolist()
         self.G, self.T = int(c[0]), int(c[1])
         self.kept_pads = int(c[3])
+        self.L0, self.prefix_len = int(c[4]), int(c[5])
         return self.G, self.T
 
 
@@ -96,7 +99,7 @@ class ReconstructionInfo(dict):
     def __init__(self, plan: Plan):
         super().__init__({f: getattr(plan, f) for f in _PLAN_FIELDS})
         self.update(B=plan.B, S=plan.S, P=plan.P, G=plan.G, T=plan.T, use_unpad=plan.use_unpad,
-                    kept_pads=plan.kept_pads)
+                    kept_pads=plan.kept_pads, L0=plan.L0, prefix_len=plan.prefix_len)
         self.plan = plan
         # Padded format with pads in the packed sequence: the same batch packed without them (same groups).
         # Attention runs there, pads taking no part (Working with Packed/Unpacked Sequences).
@@ -134,8 +137,10 @@ def group(input_ids: torch.Tensor, response_length: int, return_lists: bool = Tr
 
 def pack(input_ids: torch.Tensor, position_ids: torch.Tensor, response_length: int, prompt_groups: PromptGroups,
          unique_prompts: Optional[torch.Tensor] = None, attention_mask: Optional[torch.Tensor] = None,
-         use_unpad: bool = False):
-    """spd_pack: the deduplicated ``[1, T]`` ids and positions plus reconstruction info."""
+         use_unpad: bool = False, share_prefix: bool = False):
+    """spd_pack: the deduplicated ``[1, T]`` ids and positions plus reconstruction info.
+
+    ``share_prefix`` (spd_share_prefix) also packs the batch's shared prompt prefix once, ahead of all groups."""
     if not isinstance(prompt_groups, PromptGroups):
         raise TypeError("prompt_groups must come from group()/find_prompt_groups() (it carries the device plan)")
     plan = prompt_groups.plan
@@ -160,6 +165,9 @@ def pack(input_ids: torch.Tensor, position_ids: torch.Tensor, response_length: i
         raise ValueError("use_unpad=True needs attention_mask")
     dev = input_ids.device
     n = plan.B * plan.S
+    if share_prefix:
+        check("spd_share_prefix", lib.spd_share_prefix(_ptr(input_ids), plan.B, plan.S, int(response_length),
+                                                       ctypes.byref(plan.c), _stream(dev)))
     dids = torch.empty(n, dtype=torch.int64, device=dev)
     dpos = torch.empty(n, dtype=torch.int64, device=dev)
     ws = torch.empty(lib.spd_pack_workspace_bytes(plan.B, plan.S), dtype=torch.uint8, device=dev)
@@ -174,6 +182,7 @@ def pack(input_ids: torch.Tensor, position_ids: torch.Tensor, response_length: i
         for f in ("group_of", "grp_off", "grp_idx", "rep"):
             getattr(twin, f).copy_(getattr(plan, f))
         twin.counts[:1].copy_(plan.counts[:1])
+        twin.counts[4:5].copy_(plan.counts[4:5])       # the same shared prefix, if any
         tids = torch.empty(n, dtype=torch.int64, device=dev)
         tpos = torch.empty(n, dtype=torch.int64, device=dev)
         check("spd_pack", lib.spd_pack(_ptr(input_ids), _ptr(position_ids), mask_ptr, esz, 1, ctypes.byref(twin.c),
@@ -533,9 +542,11 @@ def find_prompt_groups(input_ids: torch.Tensor, response_length: int):
 
 
 def create_deduplicated_batch(input_ids, position_ids, response_length, prompt_groups, unique_prompts,
-                              attention_mask=None, use_unpad=False):
-    """Creating Deduplicated Batch: ``(dedup_input_ids [1,T], dedup_position_ids [1,T], reconstruction_info)``."""
-    return pack(input_ids, position_ids, response_length, prompt_groups, unique_prompts, attention_mask, use_unpad)
+                              attention_mask=None, use_unpad=False, share_prefix=False):
+    """Creating Deduplicated Batch: ``(dedup_input_ids [1,T], dedup_position_ids [1,T], reconstruction_info)``;
+    ``share_prefix`` also packs the prompts' common prefix once (prefix caching)."""
+    return pack(input_ids, position_ids, response_length, prompt_groups, unique_prompts, attention_mask, use_unpad,
+                share_prefix)
 
 
 def reconstruct_sequences(dedup_hidden: torch.Tensor, reconstruction_info: ReconstructionInfo) -> torch.Tensor:

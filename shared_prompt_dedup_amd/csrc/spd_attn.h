@@ -15,23 +15,32 @@
 
 namespace spd {
 
-// A query tile: rows [r0, r1); unmasked prompt keys [u0, u1) (empty for
-// prompt tiles); own-segment keys start at s0 (masked by the rule above).
+// A shared prefix (the prompts' common first columns, packed once ahead of
+// every group) adds one level: its rows are keys of every later row.
+//
+// A query tile: rows [r0, r1); unmasked keys [v0, v1) (the shared prefix;
+// empty without one or for the prefix's own tiles) and [u0, u1) (the group's
+// prompt; empty for prompt tiles); own-segment keys start at s0 (masked by the
+// rule above).
 // A key tile: keys [r0, r1); masked query rows [u0, u1) (the rule above);
-// unmasked query rows [s0, e0) (a prompt key tile's group responses).
-struct alignas(32) Tile {
+// unmasked query rows [s0, e0) (a prompt key tile's group responses; a prefix
+// key tile's every later row).
+struct alignas(16) Tile {
   int r0, r1;
   int u0, u1;
   int s0, e0;
   int cost;
-  int kind;   // 0 = prompt rows, 1 = response rows
+  int kind;   // 0 = prompt or prefix rows, 1 = response rows
+  int v0, v1;
+  int pad0, pad1;
 };
 
 enum TileMode { kQueryTiles = 0, kKeyTiles = 1 };
 
-// Upper bound on the tiles of one list.
+// Upper bound on the tiles of one list (a partial tile per prompt, per
+// response block and for the prefix).
 inline int64_t tile_capacity(int64_t B, int64_t T, int rows_per_tile) {
-  return (T + rows_per_tile - 1) / rows_per_tile + 2 * B + 1;
+  return (T + rows_per_tile - 1) / rows_per_tile + 2 * B + 2;
 }
 
 // Builds a tile list on the device (one block), sorted by decreasing cost so

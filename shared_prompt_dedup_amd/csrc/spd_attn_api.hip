@@ -47,7 +47,9 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
   const int tid = threadIdx.x;
   const int G = plan.counts[0];
   const int Tdev = min(plan.counts[1], T);
-  int base = 0;
+  const int Lp = min(plan.counts[5], Tdev);       // shared prefix rows [0, Lp), first in the layout
+  const int npre = (Lp + TM - 1) / TM;
+  int base = npre;
   for (int g0 = 0; g0 < G; g0 += kPlanThreads) {
     const int g = g0 + tid;
     int cnt = 0;
@@ -64,6 +66,28 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
   __syncthreads();
   const int N = min(base, cap);
   for (int i = tid; i < N; i += kPlanThreads) {
+    Tile t;
+    t.pad0 = t.pad1 = 0;
+    if (i < npre) {           // the shared prefix: its own causal keys only
+      t.r0 = i * TM;
+      t.r1 = min(Lp, t.r0 + TM);
+      t.kind = 0;
+      t.v0 = t.v1 = 0;
+      if (mode == kQueryTiles) {
+        t.u0 = t.u1 = 0;
+        t.s0 = 0;
+        t.e0 = 0;
+        t.cost = t.r1;
+      } else {
+        t.u0 = t.r0;
+        t.u1 = Lp;
+        t.s0 = Lp;
+        t.e0 = Tdev;
+        t.cost = (Lp - t.r0) + (Tdev - Lp);
+      }
+      tmp[i] = t;
+      continue;
+    }
     int lo = 0, hi = G - 1;   // last group whose first tile is <= i
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -74,17 +98,19 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
     const GroupRows r = group_rows(plan, g, G, Tdev, TM);
     const int j = i - goff[g];
     const bool prompt = j < r.np;
-    Tile t;
     t.r0 = (prompt ? r.po : r.ro) + (prompt ? j : j - r.np) * TM;
     t.r1 = min(prompt ? r.ro : r.re, t.r0 + TM);
     t.kind = prompt ? 0 : 1;
     if (mode == kQueryTiles) {
+      t.v0 = 0;
+      t.v1 = Lp;
       t.u0 = prompt ? 0 : r.po;
       t.u1 = prompt ? 0 : r.ro;
       t.s0 = plan.seg_start[t.r0];
       t.e0 = 0;
-      t.cost = (t.u1 - t.u0) + (t.r1 - t.s0);
+      t.cost = Lp + (t.u1 - t.u0) + (t.r1 - t.s0);
     } else {
+      t.v0 = t.v1 = 0;
       t.u0 = t.r0;
       t.u1 = prompt ? r.ro : segment_end(plan, t.r1 - 1);
       t.s0 = prompt ? r.ro : 0;

@@ -34,7 +34,8 @@ constexpr int kDkdvKeys = 256;  // keys per k_dkdv tile (8 waves x 32)
 // Per (head, row): nD = -sum_d dO O and nL = -lse / scale, so that
 // P = exp2(c (s + nL)) with c = scale log2(e) and s the raw score Q.K, and
 // dS = P (dP + nD); score and dP accumulators can start at nL and nD.  Per
-// row: send = one past the last row of the row's segment (prompt or response).
+// row: send = one past the last row of the row's segment (shared prefix, prompt
+// or response).
 // D and Ls have a row stride of Tp >= T + 64 so that 64-row blocks starting
 // below T never leave them; the padding rows are set to 0 and every reader
 // masks them.
@@ -70,7 +71,9 @@ __global__ void __launch_bounds__(256) k_bwd_pre(int64_t rows_x_heads, int Hq, i
       const int b = static_cast<int>(src / plan.S);
       const int64_t t = src - int64_t(b) * plan.S;
       int end;
-      if (t < plan.P) {
+      if (t < plan.counts[4]) {
+        end = plan.counts[5];          // a row of the shared prefix
+      } else if (t < plan.P) {
         const int g = plan.group_of[b];
         end = plan.prompt_off[g] + plan.prompt_len[g];
       } else {
@@ -158,15 +161,26 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
       toff[dblk][w] = swz_off<D>(row, dcol >> 3) + ((dcol & 7) << 1);
     }
 
-  const int nA = (t.u1 - t.u0 + BN - 1) / BN;
+  // Unmasked keys -- the shared prefix [v0, v1), then the group's prompt
+  // [u0, u1) -- form one virtual range [0, lenA): tile i < nA starts at virtual
+  // key i * BN and only its copy maps virtual rows to real ones.  Then the
+  // tile's own segment from s0.
+  const int lenV = t.v1 - t.v0;
+  const int lenA = lenV + (t.u1 - t.u0);
+  const int nA = (lenA + BN - 1) / BN;
   const int nB = (t.r1 - t.s0 + BN - 1) / BN;
   const int n = nA + nB;
-  auto kt_of = [&](int i) { return i < nA ? t.u0 + i * BN : t.s0 + (i - nA) * BN; };
+  auto kt_of = [&](int i) { return i < nA ? i * BN : t.s0 + (i - nA) * BN; };
 
   auto issue = [&](int i) {
     char *st = smem + (i % STAGES) * 2 * TB;
-    dma_rows<BN, D, NW>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
-    dma_rows<BN, D, NW>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
+    if (i < nA) {
+      dma_rows2<BN, D, NW>(st, k, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
+      dma_rows2<BN, D, NW>(st + TB, v, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
+    } else {
+      dma_rows<BN, D, NW>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
+      dma_rows<BN, D, NW>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
+    }
   };
   wait_vm_all();
   for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
@@ -179,7 +193,12 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
     if (qlast < qw0 || (!phaseA && kt > qlast)) continue;
     const char *Ks = smem + (i % STAGES) * 2 * TB;
     const char *Vs = Ks + TB;
-    const bool need_mask = phaseA ? (kt + BN > t.u1) : (kt + BN - 1 > qw0 || kt < seg_hi);
+    const bool need_mask = phaseA ? (kt + BN > lenA) : (kt + BN - 1 > qw0 || kt < seg_hi);
+    const char *kb_[D / 32][2];   // K^T read bases of this tile
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) kb_[dblk][w] = opaque_lds(Ks + toff[dblk][w]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = zero16(), dp = zero16();
@@ -193,7 +212,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt + 32 * kb + c_row(r, half);
-          const bool vis = phaseA ? (key < t.u1) : (key <= qrow && key >= seg_q);
+          const bool vis = phaseA ? (key < lenA) : (key <= qrow && key >= seg_q);
           s[r] = vis ? s[r] : -INFINITY;
         }
       }
@@ -208,8 +227,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
         const int ks = 2 * kb + j;
 #pragma unroll
         for (int dblk = 0; dblk < D / 32; ++dblk) {
-          const bf16x8 a =
-              ld_lds_tr_pair(Ks + toff[dblk][0] + ks * 16 * D * 2, Ks + toff[dblk][1] + ks * 16 * D * 2);
+          const bf16x8 a = ld_lds_tr_pair(kb_[dblk][0] + ks * 16 * D * 2, kb_[dblk][1] + ks * 16 * D * 2);
           acc[dblk] = mfma(a, dsf[j], acc[dblk]);
         }
       }

@@ -70,6 +70,16 @@ __device__ inline bf16x8 ld_lds_tr_pair(const char *p0, const char *p1) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// p, with the compiler unable to see through the value: per-lane LDS bases
+// are then formed once per tile and every constant step folds into the
+// instruction's offset field, instead of one precomputed sum being kept live
+// per (base, step) pair across the loop.
+__device__ inline const char *opaque_lds(const char *p) {
+  auto q = (const __attribute__((address_space(3))) char *)(p);
+  asm volatile("" : "+v"(q));
+  return (const char *)(q);
+}
+
 // Row (0..31) of register r of a 32x32 result for lane half h.
 __device__ inline int c_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -128,6 +138,33 @@ __device__ inline void dma_rows(char *tile, const __bf16 *src, int r0, int T, in
     const int chunk = slot ^ swz_of<D>(r);
     const unsigned voff = static_cast<unsigned>(min(r, rmax)) * row_bytes + (chunk << 4);
     dma16(base, voff, tile + blk * 1024);
+  }
+}
+
+// As dma_rows, for rows x0 .. x0 + ROWS - 1 of a virtual row space joining two
+// ranges: virtual row x < lenV is row v0 + x, later ones row u0 + x - lenV
+// (rows past T - 1 are clamped to it; the caller masks what it does not own).
+// Lane offsets are 32-bit from the head's first row: the host keeps
+// T * H * D * 2 below 4 GiB.
+template <int ROWS, int D, int NW>
+__device__ inline void dma_rows2(char *tile, const __bf16 *src, int x0, int lenV, int v0, int u0, int T, int H,
+                                 int hh, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int CHUNKS = ROWS * CPR;
+  static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
+  constexpr int PER_WAVE = CHUNKS / (NW * 64);
+  const __bf16 *base = src + int64_t(hh) * D;
+  const unsigned row_bytes = static_cast<unsigned>(H) * D * 2;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int blk = wave * PER_WAVE + i;
+    const int L = blk * 64 + lane;
+    const int r = L / CPR;
+    const int slot = L % CPR;
+    const int chunk = slot ^ swz_of<D>(r);
+    const int x = x0 + r;
+    const int row = min(x < lenV ? v0 + x : u0 + (x - lenV), T - 1);
+    dma16(base, static_cast<unsigned>(row) * row_bytes + (chunk << 4), tile + blk * 1024);
   }
 }
 

@@ -51,6 +51,7 @@ __global__ void __launch_bounds__(kF32Rows) k_fwd_f32(const Tile *__restrict__ t
     m = mn;
   };
   if (valid) {
+    for (int key = t.v0; key < t.v1; ++key) visit(key);
     for (int key = t.u0; key < t.u1; ++key) visit(key);
     for (int key = t.s0; key <= row; ++key)
       if (sees(key, row, seg_start)) visit(key);
@@ -117,6 +118,7 @@ __global__ void __launch_bounds__(kF32Rows) k_dq_f32(const Tile *__restrict__ ti
 #pragma unroll
     for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
   };
+  for (int key = t.v0; key < t.v1; ++key) visit(key);
   for (int key = t.u0; key < t.u1; ++key) visit(key);
   for (int key = t.s0; key <= row; ++key)
     if (sees(key, row, seg_start)) visit(key);

@@ -90,15 +90,26 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
       voff[dblk][w] = swz_off<D>(row, dcol >> 3) + ((dcol & 7) << 1);
     }
 
-  const int nA = (t.u1 - t.u0 + BN - 1) / BN;
+  // Unmasked keys -- the shared prefix [v0, v1), then the group's prompt
+  // [u0, u1) -- form one virtual range [0, lenA): tile i < nA starts at virtual
+  // key i * BN and only its copy maps virtual rows to real ones.  Then the
+  // tile's own segment from s0.
+  const int lenV = t.v1 - t.v0;
+  const int lenA = lenV + (t.u1 - t.u0);
+  const int nA = (lenA + BN - 1) / BN;
   const int nB = (t.r1 - t.s0 + BN - 1) / BN;
   const int n = nA + nB;
-  auto kt_of = [&](int i) { return i < nA ? t.u0 + i * BN : t.s0 + (i - nA) * BN; };
+  auto kt_of = [&](int i) { return i < nA ? i * BN : t.s0 + (i - nA) * BN; };
 
   auto issue = [&](int i) {
     char *st = smem + (i % STAGES) * 2 * TB;
-    dma_rows<BN, D, NW>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
-    dma_rows<BN, D, NW>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
+    if (i < nA) {
+      dma_rows2<BN, D, NW>(st, k, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
+      dma_rows2<BN, D, NW>(st + TB, v, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
+    } else {
+      dma_rows<BN, D, NW>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
+      dma_rows<BN, D, NW>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
+    }
   };
   wait_vm_all();
   for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
@@ -111,7 +122,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
     if (qlast < qw0 || (!phaseA && kt > qlast)) continue;   // nothing this wave can see
     const char *Ks = smem + (i % STAGES) * 2 * TB;
     const char *Vs = Ks + TB;
-    const bool need_mask = phaseA ? (kt + BN > t.u1) : (kt + BN - 1 > qw0 || kt < seg_hi);
+    const bool need_mask = phaseA ? (kt + BN > lenA) : (kt + BN - 1 > qw0 || kt < seg_hi);
 
     f32x16 s[2];
 #pragma unroll
@@ -127,7 +138,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt + 32 * kb + c_row(r, half);
-          const bool vis = phaseA ? (key < t.u1) : (key <= qrow && key >= seg_q);
+          const bool vis = phaseA ? (key < lenA) : (key <= qrow && key >= seg_q);
           s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
     }
@@ -154,12 +165,16 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
         l_run += p;
         pf[2 * kb + (r >> 3)][r & 7] = static_cast<__bf16>(p);
       }
+    const char *vb[D / 32][2];
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) vb[dblk][w] = opaque_lds(Vs + voff[dblk][w]);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dblk = 0; dblk < D / 32; ++dblk) {
-        const bf16x8 a =
-            ld_lds_tr_pair(Vs + voff[dblk][0] + ks * 16 * D * 2, Vs + voff[dblk][1] + ks * 16 * D * 2);
+        const bf16x8 a = ld_lds_tr_pair(vb[dblk][0] + ks * 16 * D * 2, vb[dblk][1] + ks * 16 * D * 2);
         oacc[dblk] = mfma(a, pf[ks], oacc[dblk]);
       }
   }

@@ -9,6 +9,8 @@
 #include <mutex>
 #include <vector>
 
+#include <climits>
+
 #include "spd_internal.h"
 
 namespace spd {
@@ -151,6 +153,8 @@ __global__ void __launch_bounds__(kFinalThreads) k_finalize_groups(int B, const 
   if (tid == 0) {
     plan.grp_off[G] = B;
     plan.counts[0] = G;
+    plan.counts[4] = 0;    // no shared prefix unless spd_share_prefix finds one
+    plan.counts[5] = 0;
   }
   __syncthreads();
   for (int g = tid; g < G; g += kFinalThreads) fill[g] = 0;
@@ -221,22 +225,28 @@ __global__ void __launch_bounds__(256) k_seg_lengths(int64_t S, int64_t P, const
   const int b = blockIdx.x;
   const int g = plan.group_of[b];
   const bool first = plan.rep[g] == b;
-  int r, p = 0;
+  const bool first_of_all = plan.rep[0] == b;    // packs the shared prefix, if any
+  const int64_t L0 = plan.counts[4];
+  int r, p = 0, lp = 0;
   if (unpad) {
     r = block_count_kept(mask, esz, int64_t(b) * S, P, S);
-    if (first) p = block_count_kept(mask, esz, int64_t(b) * S, 0, P);
+    if (first) p = block_count_kept(mask, esz, int64_t(b) * S, L0, P);
+    if (first_of_all && L0 > 0) lp = block_count_kept(mask, esz, int64_t(b) * S, 0, L0);
   } else {
     r = static_cast<int>(S - P);
-    p = static_cast<int>(P);
+    p = static_cast<int>(P - L0);
+    lp = static_cast<int>(L0);
   }
   if (threadIdx.x == 0) {
     plan.resp_len[b] = r;
     if (first) plan.prompt_len[g] = p;
+    if (first_of_all) plan.counts[5] = lp;
   }
 }
 
-// Single block: segment order [prompt g][members of g ascending]..., exclusive
-// scan of segment lengths -> prompt_off / resp_off, counts[1] = T.
+// Single block: segment order [shared prefix][prompt g][members of g
+// ascending]..., exclusive scan of segment lengths -> prompt_off / resp_off,
+// counts[1] = T.
 __global__ void __launch_bounds__(kFinalThreads) k_seg_offsets(int B, int32_t *__restrict__ seg, spd_plan plan) {
   __shared__ int scan_tmp[kFinalThreads / 64];
   const int G = plan.counts[0];
@@ -247,7 +257,7 @@ __global__ void __launch_bounds__(kFinalThreads) k_seg_offsets(int B, int32_t *_
     seg[i + plan.group_of[b] + 1] = plan.resp_len[b];
   }
   __syncthreads();
-  int base = 0;
+  int base = plan.counts[5];     // rows of the shared prefix come first
   for (int s0 = 0; s0 < nseg; s0 += kFinalThreads) {
     const int s = s0 + threadIdx.x;
     const int len = s < nseg ? seg[s] : 0;
@@ -312,8 +322,26 @@ __global__ void __launch_bounds__(256) k_scatter(int64_t S, int64_t P, const int
   int pads = 0;       // (b, t) mapped to no packed row (unpad mode)
   int kept_pads = 0;  // packed rows whose mask entry is 0 (padded mode with a mask)
   const bool count_kept_pads = !unpad && mask;
-  // prompt columns: kept-ness and positions come from the first member
-  for_kept_columns(mask, esz, unpad, int64_t(r) * S, 0, P, [&](int64_t t, bool kept, int rank) {
+  // shared prefix columns [0, L0): packed once, from the first sample of the
+  // first group, ahead of every group
+  const int64_t L0 = plan.counts[4];
+  if (L0 > 0) {
+    const int r0 = plan.rep[0];
+    for_kept_columns(mask, esz, unpad, int64_t(r0) * S, 0, L0, [&](int64_t t, bool kept, int rank) {
+      plan.dst[int64_t(b) * S + t] = kept ? rank : -1;
+      pads += !kept;
+      if (kept && b == r0) {
+        const int64_t s = int64_t(r0) * S + t;
+        plan.src[rank] = static_cast<int32_t>(s);
+        plan.seg_start[rank] = 0;
+        dids[rank] = ids[s];
+        dpos[rank] = pos[s];
+        if (count_kept_pads) kept_pads += !mask_at(mask, esz, s);
+      }
+    });
+  }
+  // prompt columns [L0, P): kept-ness and positions come from the first member
+  for_kept_columns(mask, esz, unpad, int64_t(r) * S, L0, P, [&](int64_t t, bool kept, int rank) {
     const int j = po + rank;
     plan.dst[int64_t(b) * S + t] = kept ? j : -1;
     pads += !kept;
@@ -410,7 +438,11 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
     const int64_t t = s - b0 * S;
     int m0 = 0, m1 = 1;
     const int32_t *members = nullptr;
-    if (t < P) {
+    bool every_sample = false;      // a shared-prefix row: read by every sample
+    if (t < plan.counts[4]) {
+      m1 = static_cast<int>(plan.B);
+      every_sample = true;
+    } else if (t < P) {
       const int g = plan.group_of[b0];
       m0 = plan.grp_off[g];
       m1 = plan.grp_off[g + 1];
@@ -425,7 +457,7 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
         if (c < vec_per_row) v[u] = in[c];
       }
       for (int m = m0; m < m1; ++m) {
-        const int64_t b = members ? members[m] : b0;
+        const int64_t b = every_sample ? m : (members ? members[m] : b0);
         u32x4 *o = out + (b * S + t) * vec_per_row;
         const bool zero = SOURCE_ONLY && b != b0;
 #pragma unroll
@@ -462,7 +494,11 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct_bwd(int64_t T, int6
     const int64_t t = s - b0 * S;
     int m0 = 0, m1 = 1;
     const int32_t *members = nullptr;
-    if (t < P) {
+    bool every_sample = false;      // a shared-prefix row: read by every sample
+    if (t < plan.counts[4]) {
+      m1 = static_cast<int>(plan.B);
+      every_sample = true;
+    } else if (t < P) {
       const int g = plan.group_of[b0];
       m0 = plan.grp_off[g];
       m1 = plan.grp_off[g + 1];
@@ -476,7 +512,7 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct_bwd(int64_t T, int6
 #pragma unroll
         for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
       for (int m = m0; m < m1; ++m) {
-        const int64_t b = members ? members[m] : b0;
+        const int64_t b = every_sample ? m : (members ? members[m] : b0);
         const int64_t cell = b * S + t;
         int64_t r = cell;
         if (to_dst) {
@@ -509,6 +545,33 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct_bwd(int64_t T, int6
   }
 }
 
+// Shared prefix: counts[4] = the number of leading prompt columns on which
+// the first members of all groups agree (0 with fewer than two groups).
+__global__ void k_prefix_init(int64_t P, spd_plan plan) {
+  if (threadIdx.x == 0) plan.counts[4] = plan.counts[0] >= 2 ? static_cast<int32_t>(P) : 0;
+}
+
+// One block per group g >= 1: its first mismatch with group 0's prompt.
+__global__ void __launch_bounds__(256) k_prefix_mismatch(const int64_t *__restrict__ ids, int64_t S, int64_t P,
+                                                         spd_plan plan) {
+  __shared__ int wmin[4];
+  const int g = blockIdx.x + 1;
+  if (g >= plan.counts[0]) return;
+  const int64_t *a = ids + int64_t(plan.rep[0]) * S;
+  const int64_t *c = ids + int64_t(plan.rep[g]) * S;
+  int first = INT_MAX;
+  for (int64_t t = threadIdx.x; t < P; t += blockDim.x)
+    if (a[t] != c[t]) first = min(first, static_cast<int>(t));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
+  if (__lane_id() == 0) wmin[threadIdx.x / 64] = first;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) first = min(first, wmin[w]);
+    if (first != INT_MAX) atomicMin(&plan.counts[4], first);
+  }
+}
+
 // Every sample its own group: the plan of the non-deduplicated batch.
 __global__ void k_singleton_groups(int B, spd_plan plan) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -521,6 +584,8 @@ __global__ void k_singleton_groups(int B, spd_plan plan) {
   if (b == 0) {
     plan.grp_off[B] = B;
     plan.counts[0] = B;
+    plan.counts[4] = 0;
+    plan.counts[5] = 0;
   }
 }
 
@@ -707,6 +772,22 @@ extern "C" spd_status spd_pack_rows_bwd(const spd_plan *plan, int64_t T, const v
                      plan->counts, static_cast<u32x4 *>(drows));
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_PACK_ROWS_BWD, st);
+  return SPD_OK;
+}
+
+extern "C" spd_status spd_share_prefix(const int64_t *input_ids, int64_t B, int64_t S, int64_t response_length,
+                                       const spd_plan *plan, void *stream) {
+  SPD_TRY(validate_plan(plan));
+  if (!input_ids || B != plan->B || S != plan->S || response_length < 0 || response_length > S ||
+      plan->P != S - response_length)
+    return SPD_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_prefix_init, dim3(1), dim3(64), 0, st, plan->P, *plan);
+  SPD_LAUNCH_CHECK();
+  if (B > 1 && plan->P > 0) {
+    hipLaunchKernelGGL(k_prefix_mismatch, dim3(unsigned(B - 1)), dim3(256), 0, st, input_ids, S, plan->P, *plan);
+    SPD_LAUNCH_CHECK();
+  }
   return SPD_OK;
 }
 

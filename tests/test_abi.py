@@ -112,6 +112,13 @@ def test_rows_calls_reject_bad_arguments():
     assert lib.spd_pack_rows_bwd(ctypes.byref(p), 5, A[12], 32, None, None) == INVALID
 
 
+def test_share_prefix_rejects_bad_arguments():
+    p = _plan()
+    assert lib.spd_share_prefix(A[12], 3, 8, 2, ctypes.byref(p), None) == INVALID   # B mismatch
+    assert lib.spd_share_prefix(A[12], 4, 8, 3, ctypes.byref(p), None) == INVALID   # P = S - response_length
+    assert lib.spd_share_prefix(None, 4, 8, 2, ctypes.byref(p), None) == INVALID
+
+
 def test_standard_mode_calls_reject_bad_arguments():
     p, q = _plan(), _plan()
     other = _plan(B=3)

@@ -48,6 +48,7 @@ class Workload:
     # (lo, hi) inclusive response-length range for right-padded variable
     # responses (packed with use_unpad=True); None = every response is full.
     resp_len_range: Optional[tuple] = None
+    shared_prefix: int = 0      # leading prompt tokens common to every prompt (0: prompts independent)
 
     @property
     def batch(self) -> int:
@@ -83,6 +84,11 @@ WORKLOADS = {
     # Backward-heavy batch: 32 = 4 x 8, prompt 4096, response 1024.
     "bwd_4x8_p4096_r1024": Workload(
         "bwd_4x8_p4096_r1024", 4, 8, 4096, 1024, 16, 8, 128, "bf16", QWEN_VOCAB, 0.5, 1004),
+    # Partially overlapping prompts: 32 = 4 x 8, four 5120-token prompts that share their first 4096 tokens
+    # (a common system prompt), response 512.  Exercises prefix sharing.
+    "prefix_4x8_s4096_p5120_r512": Workload(
+        "prefix_4x8_s4096_p5120_r512", 4, 8, 5120, 512, 16, 8, 128, "bf16", QWEN_VOCAB, 0.5, 1005,
+        shared_prefix=4096),
 }
 
 # The single-GPU workload that throughput is quoted on.
@@ -105,6 +111,11 @@ def make_batch(w: Workload, permute: bool = False, pad_id: int = 0) -> Batch:
     B, P, R = w.batch, w.prompt_len, w.response_len
     S = P + R
     prompts = rng.integers(0, w.vocab, size=(w.num_prompts, P), dtype=np.int64)
+    if w.shared_prefix:
+        L = w.shared_prefix
+        prompts[:, :L] = prompts[0, :L]
+        if L < P:   # column L differs between prompts, so the common prefix is exactly L long
+            prompts[:, L] = (prompts[0, L] + np.arange(w.num_prompts)) % w.vocab
     resps = rng.integers(0, w.vocab, size=(B, R), dtype=np.int64)
     if w.resp_len_range is not None:
         lo, hi = w.resp_len_range
