@@ -11,6 +11,8 @@
 // keeps siblings apart).  Key tiles are cut the same way.
 #pragma once
 
+#include <algorithm>
+
 #include "spd_internal.h"
 
 namespace spd {
@@ -25,6 +27,12 @@ namespace spd {
 // A key tile: keys [r0, r1); masked query rows [u0, u1) (the rule above);
 // unmasked query rows [s0, e0) (a prompt key tile's group responses; a prefix
 // key tile's every later row).
+//
+// A key tile whose reader rows are many more than a CU's fair share is cut
+// into chunks over its reader rows ([u0, u1) then [s0, e0); each chunk keeps
+// its part of both ranges); a chunk writes fp32 partial dK / dV to its slot and
+// k_dkdv_reduce adds the slots of the tile in chunk order, then scales and
+// rounds once.
 struct alignas(16) Tile {
   int r0, r1;
   int u0, u1;
@@ -32,8 +40,26 @@ struct alignas(16) Tile {
   int cost;
   int kind;   // 0 = prompt or prefix rows, 1 = response rows
   int v0, v1;
-  int pad0, pad1;
+  int slot;   // key tiles: partial-sum slot of this chunk, -1 when the tile is not split
+  int pad;
 };
+
+// The chunks of one split key tile: keys [r0, r1), slots slot0 .. slot0 + n - 1.
+struct SplitGroup {
+  int r0, r1, slot0, n;
+};
+
+// Partial-sum slots of one backward call: each holds 256 keys x Hkv x D fp32
+// for dK and for dV; at most 64, and at most 1024 / Hkv so that the slots stay
+// within 256 MiB.  Chunks hold a multiple of 64 reader rows, at most 8 per tile.
+constexpr int kMaxSplitSlots = 64;
+constexpr int kSplitSlotHeads = 1024;
+constexpr int kSplitRows = 64;
+constexpr int kMaxChunks = 8;
+inline int split_slots(int num_kv_heads) {
+  const int n = std::min(kMaxSplitSlots, kSplitSlotHeads / num_kv_heads);
+  return n >= 2 ? n : 0;
+}
 
 enum TileMode { kQueryTiles = 0, kKeyTiles = 1 };
 
@@ -46,8 +72,14 @@ inline int64_t tile_capacity(int64_t B, int64_t T, int rows_per_tile) {
 // Builds a tile list on the device (one block), sorted by decreasing cost so
 // that the heaviest tiles are dispatched first.  `tmp` and `out` hold
 // `cap` tiles, `goff` B + 1 ints of scratch; *n_out receives the count.
+// Key tiles may be split (see Tile) when `splits` is given: its groups are
+// written there and their count to *n_splits; `cap` then includes `max_slots`
+// tiles of room for the extra chunks; `blocks_per_tile` (kv heads) and `n_cu`
+// size a CU's fair share.
 spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, int *goff,
-                              Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st);
+                              Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st,
+                              SplitGroup *splits = nullptr, int *n_splits = nullptr, int max_slots = 0,
+                              int blocks_per_tile = 1, int n_cu = 0);
 
 // fp32 correctness kernels (plain arithmetic, one row per thread).
 spd_status attn_fwd_f32(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *tiles,
@@ -69,7 +101,8 @@ spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
                          const int *nq, int64_t capq, const Tile *ktiles, const int *nk, int64_t capk,
                          const void *q, const void *k, const void *v, const void *o, const float *lse,
                          const void *dout, void *dq, void *dk, void *dv, float *Dbuf, float *L2buf, int *segp,
-                         int64_t Tp, hipStream_t st);
+                         int64_t Tp, const SplitGroup *splits, const int *n_splits, int max_slots, float *part_k,
+                         float *part_v, hipStream_t st);
 
 // Row stride of the backward's per-row scalar arrays: T rounded up to 64, plus
 // one 64-row block, so that 64-row reads starting below T stay inside.

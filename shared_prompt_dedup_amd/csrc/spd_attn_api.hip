@@ -4,6 +4,7 @@
 // (prompt-to-prompt once per unique prompt; response-to-full over its prompt
 // and itself) and "Correctness & Gradients".
 #include <algorithm>
+#include <climits>
 
 #include "spd_attn.h"
 
@@ -36,12 +37,30 @@ __device__ inline GroupRows group_rows(const spd_plan &plan, int g, int G, int T
   return r;
 }
 
+// Chunks a key tile is cut into when its reader rows exceed `limit` (1: not
+// split); *rows receives the reader rows per chunk.  A key tile's reader rows
+// are its masked rows [u0, u1) followed by its unmasked rows [s0, e0).
+__device__ inline int chunks_of(const Tile &t, int limit, int *rows) {
+  const int U = (t.u1 - t.u0) + (t.e0 - t.s0);
+  if (U <= limit || U < 2 * kSplitRows) {
+    *rows = U;
+    return 1;
+  }
+  const int want = min(kMaxChunks, (U + limit - 1) / limit);
+  const int per = ((U + want - 1) / want + kSplitRows - 1) / kSplitRows * kSplitRows;
+  *rows = per;
+  return (U + per - 1) / per;
+}
+
 // One block: per-group tile counts and their exclusive scan (goff[0..G]),
 // then one thread per tile (its group found by binary search over goff),
 // then a counting sort by decreasing cost.
 __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int T, int TM, int mode, int cap,
                                                                int *__restrict__ goff, Tile *__restrict__ tmp,
-                                                               Tile *__restrict__ out, int *__restrict__ n_out) {
+                                                               Tile *__restrict__ out, int *__restrict__ n_out,
+                                                               SplitGroup *__restrict__ splits,
+                                                               int *__restrict__ n_splits, int max_slots,
+                                                               int blocks_per_tile, int n_cu) {
   __shared__ int scan_tmp[kPlanThreads / 64];
   __shared__ int hist[kBuckets];
   const int tid = threadIdx.x;
@@ -64,10 +83,10 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
   }
   if (tid == 0) goff[G] = base;
   __syncthreads();
-  const int N = min(base, cap);
+  const int N = min(base, splits ? cap - max_slots : cap);
   for (int i = tid; i < N; i += kPlanThreads) {
     Tile t;
-    t.pad0 = t.pad1 = 0;
+    t.pad = 0;
     if (i < npre) {           // the shared prefix: its own causal keys only
       t.r0 = i * TM;
       t.r1 = min(Lp, t.r0 + TM);
@@ -85,7 +104,8 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
         t.e0 = Tdev;
         t.cost = (Lp - t.r0) + (Tdev - Lp);
       }
-      tmp[i] = t;
+      t.slot = -1;
+      out[i] = t;
       continue;
     }
     int lo = 0, hi = G - 1;   // last group whose first tile is <= i
@@ -117,15 +137,111 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
       t.e0 = prompt ? r.re : 0;
       t.cost = (t.u1 - t.u0) + (t.e0 - t.s0);
     }
-    tmp[i] = t;
+    t.slot = -1;
+    out[i] = t;
   }
+  __syncthreads();
+  // When the heaviest key tile is about a CU's fair share of the blocks'
+  // reader rows or more, the in-order dispatch cannot even the CUs out: tiles
+  // above half that share are cut into chunks, the limit growing until the
+  // chunks fit the partial-sum slots.  Below that, splitting only adds the
+  // partial sums' traffic.
+  int limit = INT_MAX;
+  if (splits && n_cu > 0 && max_slots >= 2) {
+    __shared__ long long red[kPlanThreads / 64];
+    __shared__ int redmax[kPlanThreads / 64];
+    long long tot = 0;
+    int mx = 0;
+    for (int i = tid; i < N; i += kPlanThreads) {
+      tot += out[i].cost;
+      mx = max(mx, out[i].cost);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      tot += __shfl_xor(tot, off, 64);
+      mx = max(mx, __shfl_xor(mx, off, 64));
+    }
+    if (__lane_id() == 0) {
+      red[tid / 64] = tot;
+      redmax[tid / 64] = mx;
+    }
+    __syncthreads();
+    tot = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+      tot += red[w];
+      mx = max(mx, redmax[w]);
+    }
+    const long long share = tot * blocks_per_tile / n_cu;
+    long long lim = 10LL * mx >= 9LL * share ? share / 2 : LLONG_MAX;
+    lim = lim < 2048 ? 2048 : lim;
+    for (int attempt = 0; attempt < 12; ++attempt) {
+      int need = 0;
+      for (int i = tid; i < N; i += kPlanThreads) {
+        int rows;
+        const int c = chunks_of(out[i], int(lim < INT_MAX ? lim : INT_MAX), &rows);
+        need += c > 1 ? c : 0;
+      }
+      int total;
+      block_exclusive_scan(need, scan_tmp, total);
+      if (total <= max_slots) {
+        limit = int(lim < INT_MAX ? lim : INT_MAX);
+        break;
+      }
+      lim = lim / 2 * 3;
+    }
+  }
+  int M = N;
+  if (splits) {
+    // expand into tmp: tile i -> c_i chunks at positions scanned over the tiles
+    int pos_base = 0, slot_base = 0, grp_base = 0;
+    for (int i0 = 0; i0 < N; i0 += kPlanThreads) {
+      const int i = i0 + tid;
+      Tile t;
+      int rows = 0, c = 0;
+      if (i < N) {
+        t = out[i];
+        c = chunks_of(t, limit, &rows);
+      }
+      int tp, ts, tg;
+      const int pos = pos_base + block_exclusive_scan(c, scan_tmp, tp);
+      const int slot0 = slot_base + block_exclusive_scan(c > 1 ? c : 0, scan_tmp, ts);
+      const int grp = grp_base + block_exclusive_scan(c > 1 ? 1 : 0, scan_tmp, tg);
+      if (i < N) {
+        if (c == 1) {
+          tmp[pos] = t;
+        } else {
+          const int Lu = t.u1 - t.u0, U = Lu + (t.e0 - t.s0);
+          for (int j = 0; j < c; ++j) {
+            const int a = j * rows, b = min(U, a + rows);   // reader rows [a, b) of [u0, u1) ++ [s0, e0)
+            Tile ch = t;
+            ch.u0 = t.u0 + min(a, Lu);
+            ch.u1 = t.u0 + min(b, Lu);
+            ch.s0 = t.s0 + max(a - Lu, 0);
+            ch.e0 = t.s0 + max(b - Lu, 0);
+            ch.cost = b - a;
+            ch.slot = slot0 + j;
+            tmp[pos + j] = ch;
+          }
+          splits[grp] = SplitGroup{t.r0, t.r1, slot0, c};
+        }
+      }
+      pos_base += tp;
+      slot_base += ts;
+      grp_base += tg;
+    }
+    M = pos_base;
+    if (tid == 0) *n_splits = grp_base;
+  } else {
+    for (int i = tid; i < N; i += kPlanThreads) tmp[i] = out[i];
+  }
+  __syncthreads();
   // counting sort by decreasing cost (order inside a bucket is free: it only
   // changes which block runs a tile first, never a result)
   int shift = 0;
   while ((Tdev >> shift) >= kBuckets) ++shift;
   for (int i = tid; i < kBuckets; i += kPlanThreads) hist[i] = 0;
   __syncthreads();
-  for (int i = tid; i < N; i += kPlanThreads) {
+  for (int i = tid; i < M; i += kPlanThreads) {
     const int bkt = kBuckets - 1 - min(tmp[i].cost >> shift, kBuckets - 1);
     atomicAdd(&hist[bkt], 1);
   }
@@ -143,21 +259,23 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
     ex += c[e];
   }
   __syncthreads();
-  for (int i = tid; i < N; i += kPlanThreads) {
+  __syncthreads();
+  for (int i = tid; i < M; i += kPlanThreads) {
     const Tile t = tmp[i];
     const int bkt = kBuckets - 1 - min(t.cost >> shift, kBuckets - 1);
     out[atomicAdd(&hist[bkt], 1)] = t;
   }
-  if (tid == 0) *n_out = N;
+  if (tid == 0) *n_out = M;
 }
 
 }  // namespace
 
 spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, int *goff,
-                              Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st) {
+                              Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st, SplitGroup *splits,
+                              int *n_splits, int max_slots, int blocks_per_tile, int n_cu) {
   static_assert(kBuckets == 4 * kPlanThreads, "bucket scan assumes 4 buckets per thread");
   hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(kPlanThreads), 0, st, plan, int(T), rows_per_tile, int(mode),
-                     int(cap), goff, tmp, out, n_out);
+                     int(cap), goff, tmp, out, n_out, splits, n_splits, max_slots, blocks_per_tile, n_cu);
   return check_launch();
 }
 
@@ -168,7 +286,10 @@ struct AttnWs {
   int *counts = nullptr, *goff = nullptr;
   float *Dbuf = nullptr, *L2buf = nullptr;
   int *segp = nullptr;
+  SplitGroup *splits = nullptr;
+  float *part_k = nullptr, *part_v = nullptr;
   int64_t capq = 0, capk = 0, Tp = 0;
+  int slots = 0;
   size_t bytes = 0;
 };
 
@@ -176,13 +297,15 @@ int q_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : fwd_
 int dq_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dq_bf16_rows_per_tile(d); }
 int k_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dkdv_bf16_rows_per_tile(d); }
 
-// Workspace: [D: Hq*Tp floats][log2 LSE: Hq*Tp floats][seg_start copy: Tp ints]
-//            [query tiles][key tiles][scratch tiles][counts]
+// Workspace: [-D: Hq*Tp floats][-lse/scale: Hq*Tp floats][segment ends: Tp ints]
+//            [query tiles][key tiles][scratch tiles][counts][group offsets]
+//            bf16 only: [split groups][partial dK][partial dV] (slots x Hkv x 256 x D floats each)
 AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
   AttnWs w;
   const int rq = std::min(q_rows(d), dq_rows(d));
+  w.slots = d.dtype == SPD_BF16 ? split_slots(d.num_kv_heads) : 0;
   w.capq = tile_capacity(B, T, rq);
-  w.capk = tile_capacity(B, T, k_rows(d));
+  w.capk = tile_capacity(B, T, k_rows(d)) + w.slots;
   w.Tp = padded_rows(T);
   const size_t dbytes = round_up(size_t(d.num_q_heads) * size_t(w.Tp) * 4, 256);
   const size_t sbytes = round_up(size_t(w.Tp) * 4, 256);
@@ -207,6 +330,15 @@ AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
   off += 256;
   if (p) w.goff = reinterpret_cast<int *>(p + off);
   off += round_up(size_t(B + 1) * 4, 256);
+  if (w.slots) {
+    const size_t pb = size_t(w.slots) * size_t(d.num_kv_heads) * size_t(k_rows(d)) * size_t(d.head_dim) * 4;
+    if (p) w.splits = reinterpret_cast<SplitGroup *>(p + off);
+    off += round_up(size_t(w.slots) * sizeof(SplitGroup), 256);
+    if (p) w.part_k = reinterpret_cast<float *>(p + off);
+    off += pb;
+    if (p) w.part_v = reinterpret_cast<float *>(p + off);
+    off += pb;
+  }
   w.bytes = off;
   return w;
 }
@@ -270,12 +402,14 @@ extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_pl
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnWs w = carve(*desc, plan->B, T, workspace);
   SPD_TRY(launch_build_tiles(*plan, T, dq_rows(*desc), kQueryTiles, w.goff, w.tmp, w.qtiles, w.counts, w.capq, st));
-  SPD_TRY(launch_build_tiles(*plan, T, k_rows(*desc), kKeyTiles, w.goff, w.tmp, w.ktiles, w.counts + 1, w.capk, st));
+  SPD_TRY(launch_build_tiles(*plan, T, k_rows(*desc), kKeyTiles, w.goff, w.tmp, w.ktiles, w.counts + 1, w.capk, st,
+                             w.splits, w.counts + 2, w.slots, desc->num_kv_heads, device_cu_count()));
   if (desc->dtype == SPD_F32)
     return attn_bwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, w.ktiles, w.counts + 1, w.capk,
                         static_cast<const float *>(q), static_cast<const float *>(k), static_cast<const float *>(v),
                         static_cast<const float *>(o), lse, static_cast<const float *>(dout),
                         static_cast<float *>(dq), static_cast<float *>(dk), static_cast<float *>(dv), w.Dbuf, st);
   return attn_bwd_bf16(*desc, *plan, T, w.qtiles, w.counts, w.capq, w.ktiles, w.counts + 1, w.capk, q, k, v, o, lse,
-                       dout, dq, dk, dv, w.Dbuf, w.L2buf, w.segp, w.Tp, st);
+                       dout, dq, dk, dv, w.Dbuf, w.L2buf, w.segp, w.Tp, w.splits, w.counts + 2, w.slots, w.part_k,
+                       w.part_v, st);
 }

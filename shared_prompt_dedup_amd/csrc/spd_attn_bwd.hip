@@ -17,8 +17,11 @@
 //   their LSE, D and segment starts) arrive by direct-to-LDS loads, double
 //   buffered.  S = Q K^T and dP = dO V^T put one key per lane column, so P^T
 //   and dS^T feed dv += P^T dO and dk += dS^T Q directly, with dO^T and Q^T
-//   read by transposing LDS reads.  No atomics anywhere: results are bitwise
-//   repeatable.
+//   read by transposing LDS reads.  A tile the planner cut into chunks (a
+//   prompt or prefix key read by far more rows than a CU's fair share) leaves
+//   fp32 partial sums in numbered slots;
+// k_dkdv_reduce: adds each split tile's slots in chunk order.
+// No atomics anywhere: results are bitwise repeatable.
 #include "spd_attn_dev.h"
 
 namespace spd {
@@ -265,7 +268,8 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
                                                       const __bf16 *__restrict__ dout,
                                                       const float *__restrict__ Dbuf,
                                                       const int *__restrict__ send, int Tp, __bf16 *__restrict__ dk,
-                                                      __bf16 *__restrict__ dv, float scale_log2, float scale) {
+                                                      __bf16 *__restrict__ dv, float *__restrict__ part_k,
+                                                      float *__restrict__ part_v, float scale_log2, float scale) {
   constexpr int NW = kWaves, QB = kQB, BK = kDkdvKeys;   // 64 query rows per block, 256 keys per tile
   constexpr int KS = D / 16;
   constexpr int TB = QB * D * 2;                    // one Q or dO tile
@@ -430,7 +434,23 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
   }
 
   // dv / dk: register r of dblk holds key row c_row(r, half) of the wave's 32
-  // keys and column 32 dblk + col.
+  // keys and column 32 dblk + col.  A chunk of a split tile leaves unscaled
+  // fp32 sums in its slot instead.
+  if (t.slot >= 0) {
+    const int64_t sbase = (int64_t(t.slot) * Hkv + kvh) * BK;
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 32 * wave + c_row(r, half);
+        if (t.r0 + kr < t.r1) {
+          const int64_t off = (sbase + kr) * D + 32 * dblk + col;
+          part_k[off] = dka[dblk][r];
+          part_v[off] = dva[dblk][r];
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
@@ -442,6 +462,44 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
         dv[off] = static_cast<__bf16>(dva[dblk][r]);
       }
     }
+}
+
+// One block per (split tile, kv head): dK / dV of the tile's keys are the sums
+// of its chunks' slots, added in chunk order, then scaled and rounded once.
+template <int D>
+__global__ void __launch_bounds__(256) k_dkdv_reduce(const SplitGroup *__restrict__ splits,
+                                                     const int *__restrict__ n_splits, int Hkv,
+                                                     const float *__restrict__ part_k,
+                                                     const float *__restrict__ part_v, __bf16 *__restrict__ dk,
+                                                     __bf16 *__restrict__ dv, float scale) {
+  constexpr int BK = kDkdvKeys, C4 = D / 4;
+  const int gi = blockIdx.x / Hkv;
+  if (gi >= *n_splits) return;
+  const int kvh = blockIdx.x % Hkv;
+  const SplitGroup g = splits[gi];
+  const int n4 = (g.r1 - g.r0) * C4;
+  const int64_t stride = int64_t(Hkv) * BK * D;   // one slot
+  for (int e = threadIdx.x; e < n4; e += blockDim.x) {
+    const int kr = e / C4, c = 4 * (e % C4);
+    const int64_t src = (int64_t(g.slot0) * Hkv + kvh) * BK * D + int64_t(kr) * D + c;
+    f32x4 sk = *reinterpret_cast<const f32x4 *>(part_k + src);
+    f32x4 sv = *reinterpret_cast<const f32x4 *>(part_v + src);
+    for (int j = 1; j < g.n; ++j) {
+      const f32x4 ak = *reinterpret_cast<const f32x4 *>(part_k + src + j * stride);
+      const f32x4 av = *reinterpret_cast<const f32x4 *>(part_v + src + j * stride);
+      sk += ak;
+      sv += av;
+    }
+    const int64_t dst = (int64_t(g.r0 + kr) * Hkv + kvh) * D + c;
+    bf16x4 ok, ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ok[i] = static_cast<__bf16>(sk[i] * scale);
+      ov[i] = static_cast<__bf16>(sv[i]);
+    }
+    *reinterpret_cast<bf16x4 *>(dk + dst) = ok;
+    *reinterpret_cast<bf16x4 *>(dv + dst) = ov;
+  }
 }
 
 int bwd_heads_per_block(const spd_attn_desc &d) {
@@ -457,7 +515,8 @@ int dkdv_bf16_rows_per_tile(const spd_attn_desc &) { return kDkdvKeys; }
 spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *qtiles, const int *nq,
                          int64_t capq, const Tile *ktiles, const int *nk, int64_t capk, const void *q, const void *k,
                          const void *v, const void *o, const float *lse, const void *dout, void *dq, void *dk,
-                         void *dv, float *Dbuf, float *Lbuf, int *send, int64_t Tp, hipStream_t st) {
+                         void *dv, float *Dbuf, float *Lbuf, int *send, int64_t Tp, const SplitGroup *splits,
+                         const int *n_splits, int max_slots, float *part_k, float *part_v, hipStream_t st) {
   const auto *qq = static_cast<const __bf16 *>(q);
   const auto *kk = static_cast<const __bf16 *>(k);
   const auto *vv = static_cast<const __bf16 *>(v);
@@ -505,11 +564,21 @@ spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
   prof_start(SPD_K_BWD_DKDV, st);
   if (d.head_dim == 128)
     hipLaunchKernelGGL(k_dkdv<128>, gk, block, 0, st, ktiles, nk, d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv,
-                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, sl2, d.softmax_scale);
+                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, part_k, part_v, sl2, d.softmax_scale);
   else
     hipLaunchKernelGGL(k_dkdv<64>, gk, block, 0, st, ktiles, nk, d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv,
-                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, sl2, d.softmax_scale);
+                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, part_k, part_v, sl2, d.softmax_scale);
   SPD_LAUNCH_CHECK();
+  if (splits && max_slots >= 2) {
+    const dim3 gr(static_cast<unsigned>(max_slots / 2 * d.num_kv_heads));
+    if (d.head_dim == 128)
+      hipLaunchKernelGGL(k_dkdv_reduce<128>, gr, dim3(256), 0, st, splits, n_splits, d.num_kv_heads, part_k, part_v,
+                         dkk, dvv, d.softmax_scale);
+    else
+      hipLaunchKernelGGL(k_dkdv_reduce<64>, gr, dim3(256), 0, st, splits, n_splits, d.num_kv_heads, part_k, part_v,
+                         dkk, dvv, d.softmax_scale);
+    SPD_LAUNCH_CHECK();
+  }
   prof_stop(SPD_K_BWD_DKDV, st);
   return SPD_OK;
 }

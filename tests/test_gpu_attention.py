@@ -6,7 +6,8 @@
 * the full-size bf16 workloads: sampled rows and keys against the oracle's
   row-wise definition, exact gradient invariants within tolerance, and exact
   visibility probes that tolerances alone cannot see;
-* bitwise repeatability of the backward (it uses no atomics).
+* bitwise repeatability of the backward (it uses no atomics; split key tiles
+  add their partial sums in a fixed order).
 """
 import math
 
@@ -45,6 +46,15 @@ SMALL = {
     "bf16_mid_2x4_p2048_r512": _base.scaled(name="bf16_mid_2x4_p2048_r512", num_prompts=2, rollout_n=4,
                                             prompt_len=2048, response_len=512, num_q_heads=16, num_kv_heads=8,
                                             head_dim=128, dtype="bf16", sigma=0.5, vocab=151936, seed=39),
+    # one prompt whose first key tiles are read by far more rows than the batch's other tiles: the backward cuts
+    # them into chunks of reader rows (a chunk boundary inside the prompt's own rows, one straddling prompt and
+    # responses) whose fp32 partial sums are added afterwards
+    "bf16_split_chunks": _base.scaled(name="bf16_split_chunks", num_prompts=1, rollout_n=3, prompt_len=2600,
+                                      response_len=600, num_q_heads=4, num_kv_heads=2, head_dim=128, dtype="bf16",
+                                      sigma=0.5, resp_len_range=(300, 600), seed=41),
+    "bf16_split_chunks_d64": _base.scaled(name="bf16_split_chunks_d64", num_prompts=1, rollout_n=3, prompt_len=2600,
+                                          response_len=600, num_q_heads=2, num_kv_heads=1, head_dim=64,
+                                          dtype="bf16", sigma=0.5, seed=42),
     "bf16_unit_sigma": _base.scaled(name="bf16_unit_sigma", num_prompts=2, rollout_n=4, prompt_len=256,
                                     response_len=64, num_q_heads=4, num_kv_heads=2, head_dim=128, dtype="bf16",
                                     sigma=1.0, seed=38),
@@ -96,9 +106,10 @@ def test_empty_prompt_and_empty_responses():
         compare(key, to_numpy(got), ref, w.dtype)
 
 
-def test_backward_is_bitwise_repeatable():
+@pytest.mark.parametrize("name", ["bf16_gqa2_ragged_unpad", "bf16_split_chunks"])
+def test_backward_is_bitwise_repeatable(name):
     import shared_prompt_dedup_amd as spd
-    w = SMALL["bf16_gqa2_ragged_unpad"]
+    w = SMALL[name]
     bt = make_batch(w, permute=True)
     _, _, _, _, ginfo = gpu_plan(bt, True)
     _, q, k, v, do = attn_inputs(w, ginfo["T"])
