@@ -48,10 +48,10 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "5e74486c25e0448f8f2659cebe17098a27f6a64afbc4aac62b91f218fc7eec30"
+TRAFFIC_SOURCES_SHA256 = "b12cd298fb0d4953c7d5b55014384cb3129f0a80349084c488d456a163fa9174"
 TRAFFIC_KIB = {   # kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
-    "fwd": (221750, 99842), "bwd_pre": (104874, 25352), "bwd_dq": (272441, 98561), "bwd_dkdv": (623620, 98621),
-    "reconstruct": (49555, 557466), "pack_rows": (49551, 98336),
+    "fwd": (220239, 99911), "bwd_pre": (104874, 25354), "bwd_dq": (271375, 98344), "bwd_dkdv": (686735, 98558),
+    "reconstruct": (49569, 557505), "pack_rows": (49553, 98336),
 }
 
 
@@ -98,7 +98,7 @@ def cpu_baseline(w, bt, pairs_per_head, min_seconds=10.0):
         blas_threads = 1
     groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
     _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
-                                                  attention_mask=bt.attention_mask, use_unpad=use_unpad)
+                                                  attention_mask=bt.attention_mask, use_unpad=w.use_unpad)
     x = make_attn_inputs(w, info["T"])
     heads = 0
     dt = 0.0
