@@ -335,8 +335,11 @@ spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_plan *plan, i
  * the forward and dout = dL/do, writes dq [T, Hq, d], dk, dv [T, Hkv, d].
  * A prompt key's dk / dv sum over the prompt's own causal queries and every
  * response row of its group; query heads sharing a kv head add into it.
- * Accumulation is fp32 and each output is rounded once.  No atomics: results
- * are bitwise reproducible run to run.
+ * Accumulation is fp32 and each output is rounded once.  Sums run in a fixed
+ * order (a key read by very many rows is split over several blocks whose fp32
+ * partial sums are added in chunk order), so results are bitwise reproducible
+ * run to run.  The workspace (spd_attn_workspace_bytes) holds per-row
+ * statistics, the tile lists and, for bf16, the partial-sum slots.
  */
 spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T,
                               const void *q, const void *k, const void *v, const void *o,

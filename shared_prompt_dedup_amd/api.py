@@ -113,8 +113,10 @@ def group(input_ids: torch.Tensor, response_length: int, return_lists: bool = Tr
     """spd_group: samples with identical prompt ids (``input_ids [B, S]`` int64).
 
     Returns ``(prompt_groups, unique_prompts [G, P])``.  With
-    ``return_lists=False`` the groups are not read back as Python lists
-    (``prompt_groups`` is then an empty ``PromptGroups`` with the plan).
+    ``return_lists=False`` nothing is read back to the host (no
+    synchronisation): ``prompt_groups`` is an empty ``PromptGroups`` carrying
+    the plan, and ``unique_prompts`` is the ``[B, P]`` buffer whose first G
+    rows hold the unique prompts (G is ``info["G"]`` once packed).
     """
     _need_cuda(input_ids, "input_ids")
     if input_ids.dtype != torch.int64 or input_ids.dim() != 2:
@@ -126,12 +128,12 @@ def group(input_ids: torch.Tensor, response_length: int, return_lists: bool = Tr
     uniq = torch.empty((B, P), dtype=torch.int64, device=input_ids.device)
     check("spd_group", lib.spd_group(_ptr(input_ids), B, S, int(response_length), ctypes.byref(plan.c),
                                      _ptr(uniq) if P > 0 else None, _ptr(ws), ws.numel(), _stream(input_ids.device)))
+    if not return_lists:
+        return PromptGroups([], plan), uniq
     plan.G = int(plan.counts[0].item())
-    groups = []
-    if return_lists:
-        off = plan.grp_off[:plan.G + 1].cpu().tolist()
-        idx = plan.grp_idx.cpu().tolist()
-        groups = [idx[off[g]:off[g + 1]] for g in range(plan.G)]
+    off = plan.grp_off[:plan.G + 1].cpu().tolist()
+    idx = plan.grp_idx.cpu().tolist()
+    groups = [idx[off[g]:off[g + 1]] for g in range(plan.G)]
     return PromptGroups(groups, plan), uniq[:plan.G]
 
 

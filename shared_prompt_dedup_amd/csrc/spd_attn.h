@@ -30,9 +30,9 @@ namespace spd {
 //
 // A key tile whose reader rows are many more than a CU's fair share is cut
 // into chunks over its reader rows ([u0, u1) then [s0, e0); each chunk keeps
-// its part of both ranges); a chunk writes fp32 partial dK / dV to its slot and
-// k_dkdv_reduce adds the slots of the tile in chunk order, then scales and
-// rounds once.
+// its part of both ranges); a chunk writes fp32 partial dK / dV to its slot,
+// and the last of the tile's chunks to finish (per kv head) adds the slots in
+// chunk order, then scales and rounds once.
 struct alignas(16) Tile {
   int r0, r1;
   int u0, u1;
@@ -41,7 +41,7 @@ struct alignas(16) Tile {
   int kind;   // 0 = prompt or prefix rows, 1 = response rows
   int v0, v1;
   int slot;   // key tiles: partial-sum slot of this chunk, -1 when the tile is not split
-  int pad;
+  int grp;    // key tiles: index of the split tile's SplitGroup, -1 when not split
 };
 
 // The chunks of one split key tile: keys [r0, r1), slots slot0 .. slot0 + n - 1.
@@ -73,12 +73,13 @@ inline int64_t tile_capacity(int64_t B, int64_t T, int rows_per_tile) {
 // that the heaviest tiles are dispatched first.  `tmp` and `out` hold
 // `cap` tiles, `goff` B + 1 ints of scratch; *n_out receives the count.
 // Key tiles may be split (see Tile) when `splits` is given: its groups are
-// written there and their count to *n_splits; `cap` then includes `max_slots`
-// tiles of room for the extra chunks; `blocks_per_tile` (kv heads) and `n_cu`
-// size a CU's fair share.
+// written there, and the arrival counters of each (group, kv head) in
+// `arrivals` are cleared; `cap` then includes `max_slots` tiles of room for
+// the extra chunks; `blocks_per_tile` (kv heads) and `n_cu` size a CU's fair
+// share.
 spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, int *goff,
                               Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st,
-                              SplitGroup *splits = nullptr, int *n_splits = nullptr, int max_slots = 0,
+                              SplitGroup *splits = nullptr, int *arrivals = nullptr, int max_slots = 0,
                               int blocks_per_tile = 1, int n_cu = 0);
 
 // fp32 correctness kernels (plain arithmetic, one row per thread).
@@ -101,8 +102,8 @@ spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
                          const int *nq, int64_t capq, const Tile *ktiles, const int *nk, int64_t capk,
                          const void *q, const void *k, const void *v, const void *o, const float *lse,
                          const void *dout, void *dq, void *dk, void *dv, float *Dbuf, float *L2buf, int *segp,
-                         int64_t Tp, const SplitGroup *splits, const int *n_splits, int max_slots, float *part_k,
-                         float *part_v, hipStream_t st);
+                         int64_t Tp, const SplitGroup *splits, int *arrivals, float *part_k, float *part_v,
+                         hipStream_t st);
 
 // Row stride of the backward's per-row scalar arrays: T rounded up to 64, plus
 // one 64-row block, so that 64-row reads starting below T stay inside.

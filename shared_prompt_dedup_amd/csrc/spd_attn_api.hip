@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
                                                                int *__restrict__ goff, Tile *__restrict__ tmp,
                                                                Tile *__restrict__ out, int *__restrict__ n_out,
                                                                SplitGroup *__restrict__ splits,
-                                                               int *__restrict__ n_splits, int max_slots,
+                                                               int *__restrict__ arrivals, int max_slots,
                                                                int blocks_per_tile, int n_cu) {
   __shared__ int scan_tmp[kPlanThreads / 64];
   __shared__ int hist[kBuckets];
@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
   const int N = min(base, splits ? cap - max_slots : cap);
   for (int i = tid; i < N; i += kPlanThreads) {
     Tile t;
-    t.pad = 0;
+    t.grp = -1;
     if (i < npre) {           // the shared prefix: its own causal keys only
       t.r0 = i * TM;
       t.r1 = min(Lp, t.r0 + TM);
@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
     }
   }
   int M = N;
-  if (splits) {
+  if (splits && limit != INT_MAX) {
     // expand into tmp: tile i -> c_i chunks at positions scanned over the tiles
     int pos_base = 0, slot_base = 0, grp_base = 0;
     for (int i0 = 0; i0 < N; i0 += kPlanThreads) {
@@ -220,9 +220,11 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
             ch.e0 = t.s0 + max(b - Lu, 0);
             ch.cost = b - a;
             ch.slot = slot0 + j;
+            ch.grp = grp;
             tmp[pos + j] = ch;
           }
           splits[grp] = SplitGroup{t.r0, t.r1, slot0, c};
+          for (int h = 0; h < blocks_per_tile; ++h) arrivals[grp * blocks_per_tile + h] = 0;
         }
       }
       pos_base += tp;
@@ -230,7 +232,6 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
       grp_base += tg;
     }
     M = pos_base;
-    if (tid == 0) *n_splits = grp_base;
   } else {
     for (int i = tid; i < N; i += kPlanThreads) tmp[i] = out[i];
   }
@@ -272,10 +273,10 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
 
 spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, int *goff,
                               Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st, SplitGroup *splits,
-                              int *n_splits, int max_slots, int blocks_per_tile, int n_cu) {
+                              int *arrivals, int max_slots, int blocks_per_tile, int n_cu) {
   static_assert(kBuckets == 4 * kPlanThreads, "bucket scan assumes 4 buckets per thread");
   hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(kPlanThreads), 0, st, plan, int(T), rows_per_tile, int(mode),
-                     int(cap), goff, tmp, out, n_out, splits, n_splits, max_slots, blocks_per_tile, n_cu);
+                     int(cap), goff, tmp, out, n_out, splits, arrivals, max_slots, blocks_per_tile, n_cu);
   return check_launch();
 }
 
@@ -287,6 +288,7 @@ struct AttnWs {
   float *Dbuf = nullptr, *L2buf = nullptr;
   int *segp = nullptr;
   SplitGroup *splits = nullptr;
+  int *arrivals = nullptr;
   float *part_k = nullptr, *part_v = nullptr;
   int64_t capq = 0, capk = 0, Tp = 0;
   int slots = 0;
@@ -299,7 +301,8 @@ int k_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dkdv
 
 // Workspace: [-D: Hq*Tp floats][-lse/scale: Hq*Tp floats][segment ends: Tp ints]
 //            [query tiles][key tiles][scratch tiles][counts][group offsets]
-//            bf16 only: [split groups][partial dK][partial dV] (slots x Hkv x 256 x D floats each)
+//            bf16 only: [split groups][arrival counters: slots x Hkv ints]
+//                       [partial dK][partial dV] (slots x Hkv x 256 x D floats each)
 AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
   AttnWs w;
   const int rq = std::min(q_rows(d), dq_rows(d));
@@ -334,6 +337,8 @@ AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
     const size_t pb = size_t(w.slots) * size_t(d.num_kv_heads) * size_t(k_rows(d)) * size_t(d.head_dim) * 4;
     if (p) w.splits = reinterpret_cast<SplitGroup *>(p + off);
     off += round_up(size_t(w.slots) * sizeof(SplitGroup), 256);
+    if (p) w.arrivals = reinterpret_cast<int *>(p + off);
+    off += round_up(size_t(w.slots) * size_t(d.num_kv_heads) * 4, 256);
     if (p) w.part_k = reinterpret_cast<float *>(p + off);
     off += pb;
     if (p) w.part_v = reinterpret_cast<float *>(p + off);
@@ -403,13 +408,13 @@ extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_pl
   AttnWs w = carve(*desc, plan->B, T, workspace);
   SPD_TRY(launch_build_tiles(*plan, T, dq_rows(*desc), kQueryTiles, w.goff, w.tmp, w.qtiles, w.counts, w.capq, st));
   SPD_TRY(launch_build_tiles(*plan, T, k_rows(*desc), kKeyTiles, w.goff, w.tmp, w.ktiles, w.counts + 1, w.capk, st,
-                             w.splits, w.counts + 2, w.slots, desc->num_kv_heads, device_cu_count()));
+                             w.splits, w.arrivals, w.slots, desc->num_kv_heads, device_cu_count()));
   if (desc->dtype == SPD_F32)
     return attn_bwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, w.ktiles, w.counts + 1, w.capk,
                         static_cast<const float *>(q), static_cast<const float *>(k), static_cast<const float *>(v),
                         static_cast<const float *>(o), lse, static_cast<const float *>(dout),
                         static_cast<float *>(dq), static_cast<float *>(dk), static_cast<float *>(dv), w.Dbuf, st);
   return attn_bwd_bf16(*desc, *plan, T, w.qtiles, w.counts, w.capq, w.ktiles, w.counts + 1, w.capk, q, k, v, o, lse,
-                       dout, dq, dk, dv, w.Dbuf, w.L2buf, w.segp, w.Tp, w.splits, w.counts + 2, w.slots, w.part_k,
-                       w.part_v, st);
+                       dout, dq, dk, dv, w.Dbuf, w.L2buf, w.segp, w.Tp, w.splits, w.arrivals, w.part_k, w.part_v,
+                       st);
 }

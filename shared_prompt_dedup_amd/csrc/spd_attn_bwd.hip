@@ -19,9 +19,9 @@
 //   and dS^T feed dv += P^T dO and dk += dS^T Q directly, with dO^T and Q^T
 //   read by transposing LDS reads.  A tile the planner cut into chunks (a
 //   prompt or prefix key read by far more rows than a CU's fair share) leaves
-//   fp32 partial sums in numbered slots;
-// k_dkdv_reduce: adds each split tile's slots in chunk order.
-// No atomics anywhere: results are bitwise repeatable.
+//   fp32 partial sums in numbered slots; an arrival counter per (tile, kv
+//   head) elects the last chunk to finish, which adds the slots in chunk
+//   order.  No float atomics: results are bitwise repeatable.
 #include "spd_attn_dev.h"
 
 namespace spd {
@@ -268,7 +268,8 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
                                                       const __bf16 *__restrict__ dout,
                                                       const float *__restrict__ Dbuf,
                                                       const int *__restrict__ send, int Tp, __bf16 *__restrict__ dk,
-                                                      __bf16 *__restrict__ dv, float *__restrict__ part_k,
+                                                      __bf16 *__restrict__ dv, const SplitGroup *__restrict__ splits,
+                                                      int *__restrict__ arrivals, float *__restrict__ part_k,
                                                       float *__restrict__ part_v, float scale_log2, float scale) {
   constexpr int NW = kWaves, QB = kQB, BK = kDkdvKeys;   // 64 query rows per block, 256 keys per tile
   constexpr int KS = D / 16;
@@ -435,7 +436,8 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
 
   // dv / dk: register r of dblk holds key row c_row(r, half) of the wave's 32
   // keys and column 32 dblk + col.  A chunk of a split tile leaves unscaled
-  // fp32 sums in its slot instead.
+  // fp32 sums in its slot instead; the tile's last chunk to arrive (for this kv
+  // head) adds all its chunks' slots in chunk order.
   if (t.slot >= 0) {
     const int64_t sbase = (int64_t(t.slot) * Hkv + kvh) * BK;
 #pragma unroll
@@ -449,6 +451,36 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
           part_v[off] = dva[dblk][r];
         }
       }
+    __shared__ int is_last;
+    const SplitGroup g = splits[t.grp];
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) is_last = atomicAdd(&arrivals[t.grp * Hkv + kvh], 1) == g.n - 1;
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    constexpr int C4 = D / 4;
+    const int64_t stride = int64_t(Hkv) * BK * D;   // one slot
+    const int64_t src0 = (int64_t(g.slot0) * Hkv + kvh) * BK * D;
+    for (int e = threadIdx.x; e < (t.r1 - t.r0) * C4; e += NW * 64) {
+      const int kr = e / C4, c = 4 * (e % C4);
+      const int64_t src = src0 + int64_t(kr) * D + c;
+      f32x4 sk = *reinterpret_cast<const f32x4 *>(part_k + src);
+      f32x4 sv = *reinterpret_cast<const f32x4 *>(part_v + src);
+      for (int j = 1; j < g.n; ++j) {
+        sk += *reinterpret_cast<const f32x4 *>(part_k + src + j * stride);
+        sv += *reinterpret_cast<const f32x4 *>(part_v + src + j * stride);
+      }
+      const int64_t dst = (int64_t(t.r0 + kr) * Hkv + kvh) * D + c;
+      bf16x4 ok, ov;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ok[i] = static_cast<__bf16>(sk[i] * scale);
+        ov[i] = static_cast<__bf16>(sv[i]);
+      }
+      *reinterpret_cast<bf16x4 *>(dk + dst) = ok;
+      *reinterpret_cast<bf16x4 *>(dv + dst) = ov;
+    }
     return;
   }
 #pragma unroll
@@ -462,44 +494,6 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
         dv[off] = static_cast<__bf16>(dva[dblk][r]);
       }
     }
-}
-
-// One block per (split tile, kv head): dK / dV of the tile's keys are the sums
-// of its chunks' slots, added in chunk order, then scaled and rounded once.
-template <int D>
-__global__ void __launch_bounds__(256) k_dkdv_reduce(const SplitGroup *__restrict__ splits,
-                                                     const int *__restrict__ n_splits, int Hkv,
-                                                     const float *__restrict__ part_k,
-                                                     const float *__restrict__ part_v, __bf16 *__restrict__ dk,
-                                                     __bf16 *__restrict__ dv, float scale) {
-  constexpr int BK = kDkdvKeys, C4 = D / 4;
-  const int gi = blockIdx.x / Hkv;
-  if (gi >= *n_splits) return;
-  const int kvh = blockIdx.x % Hkv;
-  const SplitGroup g = splits[gi];
-  const int n4 = (g.r1 - g.r0) * C4;
-  const int64_t stride = int64_t(Hkv) * BK * D;   // one slot
-  for (int e = threadIdx.x; e < n4; e += blockDim.x) {
-    const int kr = e / C4, c = 4 * (e % C4);
-    const int64_t src = (int64_t(g.slot0) * Hkv + kvh) * BK * D + int64_t(kr) * D + c;
-    f32x4 sk = *reinterpret_cast<const f32x4 *>(part_k + src);
-    f32x4 sv = *reinterpret_cast<const f32x4 *>(part_v + src);
-    for (int j = 1; j < g.n; ++j) {
-      const f32x4 ak = *reinterpret_cast<const f32x4 *>(part_k + src + j * stride);
-      const f32x4 av = *reinterpret_cast<const f32x4 *>(part_v + src + j * stride);
-      sk += ak;
-      sv += av;
-    }
-    const int64_t dst = (int64_t(g.r0 + kr) * Hkv + kvh) * D + c;
-    bf16x4 ok, ov;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ok[i] = static_cast<__bf16>(sk[i] * scale);
-      ov[i] = static_cast<__bf16>(sv[i]);
-    }
-    *reinterpret_cast<bf16x4 *>(dk + dst) = ok;
-    *reinterpret_cast<bf16x4 *>(dv + dst) = ov;
-  }
 }
 
 int bwd_heads_per_block(const spd_attn_desc &d) {
@@ -516,7 +510,7 @@ spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
                          int64_t capq, const Tile *ktiles, const int *nk, int64_t capk, const void *q, const void *k,
                          const void *v, const void *o, const float *lse, const void *dout, void *dq, void *dk,
                          void *dv, float *Dbuf, float *Lbuf, int *send, int64_t Tp, const SplitGroup *splits,
-                         const int *n_splits, int max_slots, float *part_k, float *part_v, hipStream_t st) {
+                         int *arrivals, float *part_k, float *part_v, hipStream_t st) {
   const auto *qq = static_cast<const __bf16 *>(q);
   const auto *kk = static_cast<const __bf16 *>(k);
   const auto *vv = static_cast<const __bf16 *>(v);
@@ -564,21 +558,13 @@ spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
   prof_start(SPD_K_BWD_DKDV, st);
   if (d.head_dim == 128)
     hipLaunchKernelGGL(k_dkdv<128>, gk, block, 0, st, ktiles, nk, d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv,
-                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, part_k, part_v, sl2, d.softmax_scale);
+                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, splits, arrivals, part_k, part_v, sl2,
+                       d.softmax_scale);
   else
     hipLaunchKernelGGL(k_dkdv<64>, gk, block, 0, st, ktiles, nk, d.num_q_heads, d.num_kv_heads, int(T), qq, kk, vv,
-                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, part_k, part_v, sl2, d.softmax_scale);
+                       Lbuf, dd, Dbuf, send, int(Tp), dkk, dvv, splits, arrivals, part_k, part_v, sl2,
+                       d.softmax_scale);
   SPD_LAUNCH_CHECK();
-  if (splits && max_slots >= 2) {
-    const dim3 gr(static_cast<unsigned>(max_slots / 2 * d.num_kv_heads));
-    if (d.head_dim == 128)
-      hipLaunchKernelGGL(k_dkdv_reduce<128>, gr, dim3(256), 0, st, splits, n_splits, d.num_kv_heads, part_k, part_v,
-                         dkk, dvv, d.softmax_scale);
-    else
-      hipLaunchKernelGGL(k_dkdv_reduce<64>, gr, dim3(256), 0, st, splits, n_splits, d.num_kv_heads, part_k, part_v,
-                         dkk, dvv, d.softmax_scale);
-    SPD_LAUNCH_CHECK();
-  }
   prof_stop(SPD_K_BWD_DKDV, st);
   return SPD_OK;
 }

@@ -6,7 +6,7 @@
 * the full-size bf16 workloads: sampled rows and keys against the oracle's
   row-wise definition, exact gradient invariants within tolerance, and exact
   visibility probes that tolerances alone cannot see;
-* bitwise repeatability of the backward (it uses no atomics; split key tiles
+* bitwise repeatability of the backward (no float atomics; split key tiles
   add their partial sums in a fixed order).
 """
 import math
