@@ -210,6 +210,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
         s = mfma(ld_lds8(Ks + roff[ks] + kb * 32 * D * 2), qf[ks], s);
         dp = mfma(ld_lds8(Vs + roff[ks] + kb * 32 * D * 2), df[ks], dp);
       }
+      sched_reads_ahead<3, 2 * KS, 1>();
       if (need_mask) {
         keep_branch();
 #pragma unroll
@@ -234,6 +235,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
           acc[dblk] = mfma(a, dsf[j], acc[dblk]);
         }
       }
+      sched_reads_ahead<2, 2 * (D / 32), 2>();
     }
   }
 
@@ -399,6 +401,14 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
         s = mfma(ld_lds8(Qm + roff[ks]), kf[ks], s);
         dp = mfma(ld_lds8(Dm + roff[ks]), ld_lds8(Vw + roff[ks]), dp);
       }
+      // the 8 statistics reads, then Q / dO / V operands two steps (4 MFMAs) ahead
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 + 3 * 2, 0);
+#pragma unroll
+      for (int j = 0; j < KS - 2; ++j) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 3, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
       // every (row, key) of the 32 x 32 block visible: rows inside the range,
       // and for masked rows all past the wave's last key and before the
       // earliest segment end among its keys
@@ -431,6 +441,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
           dva[dblk] = mfma(pf[j], bdo, dva[dblk]);
           dka[dblk] = mfma(dsf[j], bq, dka[dblk]);
         }
+      sched_reads_ahead<2, 4 * (D / 32), 2>();
     }
   }
 

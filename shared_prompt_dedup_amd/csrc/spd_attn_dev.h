@@ -210,5 +210,23 @@ __device__ inline void keep_branch() { asm volatile(""); }
 
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Instruction classes of the scheduler's group barriers.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Orders the scheduling region it ends: N matrix-core instructions, each
+// with R LDS operand reads, the reads issued A MFMAs ahead of their use (the
+// compiler otherwise waits on each read right before its MFMA).
+template <int A, int N, int R>
+__device__ inline void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, A * R, 0);
+#pragma unroll
+  for (int j = 0; j < N - A; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, A, 0);
+}
+
 }  // namespace dev
 }  // namespace spd

@@ -27,6 +27,7 @@ using namespace dev;
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBN = 64;
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kReadsAhead = 3;         // MFMAs an LDS operand read runs ahead of its use
 
 template <int D, int HPW>
 __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__ tiles,
@@ -131,6 +132,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) s[kb] = mfma(ld_lds8(Ks + koff[ks] + kb * 32 * D * 2), qf[ks], s[kb]);
     }
+    sched_reads_ahead<kReadsAhead, 2 * KS, 1>();
     if (need_mask) {
       keep_branch();
 #pragma unroll
@@ -177,6 +179,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
         const bf16x8 a = ld_lds_tr_pair(vb[dblk][0] + ks * 16 * D * 2, vb[dblk][1] + ks * 16 * D * 2);
         oacc[dblk] = mfma(a, pf[ks], oacc[dblk]);
       }
+    sched_reads_ahead<kReadsAhead, 4 * (D / 32), 2>();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
