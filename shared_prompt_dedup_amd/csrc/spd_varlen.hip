@@ -3,16 +3,17 @@
 // either read off a block-diagonal [total_q, total_kv] mask or taken from a
 // plan (the two attention calls of Phase 2, "Split Attention Optimization").
 //
-// Mask conversion, three launches (each reads what the previous one wrote):
-//   k_row_extent    one wave per row: first visible key, one past the last;
-//   k_mask_owner    one block, rows from the end: the block a row belongs to is
-//                   named by the first key of the nearest row at or after it
-//                   that sees any key (a suffix scan with "leftmost non-empty",
-//                   an associative operator);
-//   k_mask_blocks   one block, rows in order: a block starts where that name
-//                   changes; exclusive scan of the starts gives the indices;
-//   k_mask_check    one thread per row: rows whose keys leave their block are
-//                   counted, and each block's lengths feed the maxima.
+// Mask conversion, two launches:
+//   k_row_extent    one wave per row: first visible key, one past the last
+//                   (16 bytes per lane when rows are 16-byte multiples);
+//   k_mask_scan     one block, three passes: rows from the end, the block a
+//                   row belongs to is named by the first key of the nearest row
+//                   at or after it that sees any key (a suffix scan with
+//                   "leftmost non-empty", an associative operator); rows in
+//                   order, a block starts where that name changes and an
+//                   exclusive scan of the starts numbers them; then rows whose
+//                   keys leave their block are counted and each block's
+//                   lengths feed the maxima.
 #include <algorithm>
 #include <climits>
 
@@ -22,6 +23,7 @@ namespace spd {
 namespace {
 
 constexpr int kScan = 1024;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline int wave_max(int v) {
 #pragma unroll
@@ -35,7 +37,38 @@ __device__ inline int wave_min(int v) {
   return v;
 }
 
-// A key is visible when any byte of its esz-byte element is non-zero.
+// A key is visible when any byte of its esz-byte element is non-zero.  Rows
+// whose byte length is a multiple of 16 are read 16 bytes per lane.
+__global__ void __launch_bounds__(256) k_row_extent16(const u32x4 *__restrict__ mask, int64_t Tq, int row_vecs,
+                                                      int esz, int32_t *__restrict__ first,
+                                                      int32_t *__restrict__ last) {
+  const int lane = __lane_id();
+  const int64_t nwaves = int64_t(gridDim.x) * 4;
+  for (int64_t r = int64_t(blockIdx.x) * 4 + threadIdx.x / 64; r < Tq; r += nwaves) {
+    const u32x4 *row = mask + r * int64_t(row_vecs);
+    int lo = INT_MAX, hi = -1;
+#pragma unroll 4
+    for (int c = lane; c < row_vecs; c += 64) {
+      const u32x4 v = __builtin_nontemporal_load(row + c);
+      const unsigned w[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (w[j]) {     // little endian: byte k of the word is bits 8k .. 8k + 7
+          const int b0 = 16 * c + 4 * j;
+          lo = min(lo, b0 + (__builtin_ctz(w[j]) >> 3));
+          hi = max(hi, b0 + ((31 - __builtin_clz(w[j])) >> 3));
+        }
+      }
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+      first[r] = hi < 0 ? INT_MAX : lo / esz;
+      last[r] = hi < 0 ? 0 : hi / esz + 1;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) k_row_extent(const unsigned char *__restrict__ mask, int64_t Tq,
                                                     int row_bytes, int esz, int32_t *__restrict__ first,
                                                     int32_t *__restrict__ last) {
@@ -59,20 +92,77 @@ __global__ void __launch_bounds__(256) k_row_extent(const unsigned char *__restr
   }
 }
 
-__global__ void __launch_bounds__(kScan) k_mask_owner(int Tq, const int32_t *__restrict__ first,
-                                                      int32_t *__restrict__ owner) {
-  __shared__ int lds[kScan / 64];
+// The three passes below run in one block (k_mask_scan), each reading what
+// the previous one wrote to global memory after a block barrier.  Each
+// thread takes kItems consecutive rows: one block-wide scan per
+// kScan * kItems rows.
+constexpr int kItems = 16;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// A thread's kItems consecutive values from row r0 on (16-byte loads when all
+// are in range; the arrays start 256-byte aligned and r0 is a multiple of 16).
+__device__ inline void load_items(const int32_t *__restrict__ a, int r0, int Tq, int fill, int (&v)[kItems]) {
+  if (r0 + kItems <= Tq) {
+#pragma unroll
+    for (int q = 0; q < kItems / 4; ++q) {
+      const i32x4 x = *reinterpret_cast<const i32x4 *>(a + r0 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) v[j] = r0 + j < Tq ? a[r0 + j] : fill;
+  }
+}
+
+__device__ inline void store_items(int32_t *__restrict__ a, int r0, int Tq, const int (&v)[kItems]) {
+  if (r0 + kItems <= Tq) {
+#pragma unroll
+    for (int q = 0; q < kItems / 4; ++q) {
+      const i32x4 x = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+      *reinterpret_cast<i32x4 *>(a + r0 + 4 * q) = x;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kItems; ++j)
+      if (r0 + j < Tq) a[r0 + j] = v[j];
+  }
+}
+
+__device__ inline int block_max(int v, int *lds) {
+  v = wave_max(v);
+  __syncthreads();
+  if (__lane_id() == 0) lds[threadIdx.x / 64] = v;
+  __syncthreads();
+  int m = lds[0];
+  for (int w = 1; w < kScan / 64; ++w) m = max(m, lds[w]);
+  return m;
+}
+
+// owner[r]: first visible key of the nearest row at or after r that sees any
+// key (INT_MAX if none): a suffix scan with leftmost(a, b) = a unless a is
+// empty, else b.
+__device__ void mask_owner_pass(int Tq, const int32_t *__restrict__ first, int32_t *__restrict__ owner, int *lds) {
   const int lane = __lane_id(), wid = threadIdx.x / 64;
-  // leftmost(a, b) = a unless a is empty (INT_MAX), else b
+  constexpr int span = kScan * kItems;
   int carry = INT_MAX;
-  for (int c0 = (Tq - 1) / kScan * kScan; c0 >= 0; c0 -= kScan) {
-    const int r = c0 + threadIdx.x;
-    int v = r < Tq ? first[r] : INT_MAX;
+  for (int c0 = (Tq - 1) / span * span; c0 >= 0; c0 -= span) {
+    const int r0 = c0 + threadIdx.x * kItems;
+    int vals[kItems];
+    load_items(first, r0, Tq, INT_MAX, vals);
+    int agg = INT_MAX;
+#pragma unroll
+    for (int j = kItems - 1; j >= 0; --j)
+      if (vals[j] != INT_MAX) agg = vals[j];
+    int v = agg;          // leftmost non-empty of lanes lane .. 63
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int n = __shfl_down(v, off, 64);
       if (lane + off < 64 && v == INT_MAX) v = n;
     }
+    int later = __shfl_down(v, 1, 64);     // of lanes lane + 1 .. 63
+    if (lane == 63) later = INT_MAX;
     __syncthreads();
     if (lane == 0) lds[wid] = v;
     __syncthreads();
@@ -82,69 +172,125 @@ __global__ void __launch_bounds__(kScan) k_mask_owner(int Tq, const int32_t *__r
       if (w == wid + 1) after = all;
     }
     if (wid == kScan / 64 - 1) after = carry;
-    if (r < Tq) owner[r] = v != INT_MAX ? v : after;
+    int cur = later != INT_MAX ? later : after;
+#pragma unroll
+    for (int j = kItems - 1; j >= 0; --j) {
+      if (vals[j] != INT_MAX) cur = vals[j];
+      vals[j] = cur;
+    }
+    store_items(owner, r0, Tq, vals);
     carry = all;
   }
 }
 
-__global__ void __launch_bounds__(kScan) k_mask_blocks(int Tq, const int32_t *__restrict__ owner,
-                                                       const int32_t *__restrict__ last, int32_t *__restrict__ cu_q,
-                                                       int32_t *__restrict__ cu_k, int32_t *__restrict__ stats) {
-  __shared__ int lds[kScan / 64];
+// A block starts where the owner changes; an exclusive scan of the starts
+// numbers them.  Returns the block count; cu_q[n], cu_k[n] close the lists.
+// owner[r0] of each thread's first row r0 is replaced by the index of r0's
+// block (no thread reads it again: a thread reads its own rows and the row
+// before them).
+__device__ int mask_blocks_pass(int Tq, int32_t *__restrict__ owner, const int32_t *__restrict__ last,
+                                int32_t *__restrict__ cu_q, int32_t *__restrict__ cu_k, int *lds) {
+  constexpr int span = kScan * kItems;
   int base = 0, far = 0;
-  for (int c0 = 0; c0 < Tq; c0 += kScan) {
-    const int r = c0 + threadIdx.x;
-    const int o = r < Tq ? owner[r] : INT_MAX;
-    const bool start = o != INT_MAX && (r == 0 || owner[r - 1] != o);
-    if (r < Tq) far = max(far, last[r]);
+  for (int c0 = 0; c0 < Tq; c0 += span) {
+    const int r0 = c0 + threadIdx.x * kItems;
+    int prev = r0 > 0 && r0 - 1 < Tq ? owner[r0 - 1] : INT_MAX;
+    const int prev0 = prev;
+    int vals[kItems], lv[kItems];
+    load_items(owner, r0, Tq, INT_MAX, vals);
+    load_items(last, r0, Tq, 0, lv);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      const int r = r0 + j;
+      far = max(far, lv[j]);
+      cnt += (vals[j] != INT_MAX && (r == 0 || prev != vals[j])) ? 1 : 0;
+      prev = vals[j];
+    }
     int total;
-    const int idx = base + block_exclusive_scan(start ? 1 : 0, lds, total);
-    if (start) {
-      cu_q[idx] = r;
-      cu_k[idx] = o;
+    int idx = base + block_exclusive_scan(cnt, lds, total);
+    prev = prev0;
+    if (r0 < Tq) owner[r0] = (vals[0] != INT_MAX && (r0 == 0 || prev0 != vals[0])) ? idx : idx - 1;
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      const int r = r0 + j;
+      if (vals[j] != INT_MAX && (r == 0 || prev != vals[j])) {
+        cu_q[idx] = r;
+        cu_k[idx] = vals[j];
+        ++idx;
+      }
+      prev = vals[j];
     }
     base += total;
   }
-  __syncthreads();
-  far = wave_max(far);
-  if (__lane_id() == 0) lds[threadIdx.x / 64] = far;
-  __syncthreads();
+  far = block_max(far, lds);
   if (threadIdx.x == 0) {
-    for (int w = 0; w < kScan / 64; ++w) far = max(far, lds[w]);
-    const int n = base;
-    if (n > 0) {
-      cu_q[n] = Tq;
-      cu_k[n] = far;
+    if (base > 0) {
+      cu_q[base] = Tq;
+      cu_k[base] = far;
     } else {
       cu_q[0] = 0;
       cu_k[0] = 0;
     }
+  }
+  return base;
+}
+
+// Longest blocks, and rows whose visible keys leave their block's key range.
+// blk[r0]: index of the block of each thread's first row (mask_blocks_pass).
+__device__ void mask_check_pass(int Tq, int n, const int32_t *__restrict__ first, const int32_t *__restrict__ last,
+                                const int32_t *__restrict__ blk, const int32_t *__restrict__ cu_q,
+                                const int32_t *__restrict__ cu_k, int32_t *__restrict__ stats, int *lds) {
+  int mq = 0, mk = 0, bad = 0;
+  if (n > 0) {
+    for (int r0 = threadIdx.x * kItems; r0 < Tq; r0 += kScan * kItems) {
+      int f[kItems], l[kItems];
+      load_items(first, r0, Tq, INT_MAX, f);
+      load_items(last, r0, Tq, 0, l);
+      int i = blk[r0];                     // cu_q[i] <= r0 < cu_q[i + 1]
+      int qs = cu_q[i], qe = cu_q[i + 1], ks = cu_k[i], ke = cu_k[i + 1];
+#pragma unroll
+      for (int j = 0; j < kItems; ++j) {
+        const int r = r0 + j;
+        if (r < Tq) {
+          if (r == qe) {                   // the next block starts here
+            ++i;
+            qs = qe;
+            ks = ke;
+            qe = cu_q[i + 1];
+            ke = cu_k[i + 1];
+          }
+          if (r == qs) {
+            mq = max(mq, qe - qs);
+            mk = max(mk, ke - ks);
+          }
+          bad += (f[j] != INT_MAX && (f[j] != ks || l[j] > ke)) ? 1 : 0;
+        }
+      }
+    }
+  }
+  mq = block_max(mq, lds);
+  mk = block_max(mk, lds);
+  int tot;
+  block_exclusive_scan(bad, lds, tot);
+  if (threadIdx.x == 0) {
     stats[0] = n;
-    stats[1] = 0;
-    stats[2] = 0;
-    stats[3] = 0;
+    stats[1] = mq;
+    stats[2] = mk;
+    stats[3] = tot;
   }
 }
 
-__global__ void __launch_bounds__(256) k_mask_check(int Tq, const int32_t *__restrict__ first,
-                                                    const int32_t *__restrict__ last,
-                                                    const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k,
-                                                    int32_t *__restrict__ stats) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  const int n = stats[0];
-  if (r >= Tq || n == 0) return;
-  int lo = 0, hi = n - 1;          // block i with cu_q[i] <= r < cu_q[i + 1]
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (cu_q[mid] <= r) lo = mid;
-    else hi = mid - 1;
-  }
-  const int i = lo;
-  if (cu_q[i] == r) {
-    atomicMax(&stats[1], cu_q[i + 1] - cu_q[i]);
-    atomicMax(&stats[2], cu_k[i + 1] - cu_k[i]);
-  }
-  if (first[r] != INT_MAX && (first[r] != cu_k[i] || last[r] > cu_k[i + 1])) atomicAdd(&stats[3], 1);
+__global__ void __launch_bounds__(kScan) k_mask_scan(int Tq, const int32_t *__restrict__ first,
+                                                     const int32_t *__restrict__ last, int32_t *__restrict__ owner,
+                                                     int32_t *__restrict__ cu_q, int32_t *__restrict__ cu_k,
+                                                     int32_t *__restrict__ stats) {
+  __shared__ int lds[kScan / 64];
+  mask_owner_pass(Tq, first, owner, lds);
+  __syncthreads();
+  const int n = mask_blocks_pass(Tq, owner, last, cu_q, cu_k, lds);
+  __syncthreads();
+  mask_check_pass(Tq, n, first, last, owner, cu_q, cu_k, stats, lds);
 }
 
 // Exclusive scans of a plan's segment lengths: prompts [G], responses [B] and
@@ -220,6 +366,7 @@ extern "C" spd_status spd_mask_to_varlen(const void *mask, int32_t mask_elem_byt
     return SPD_ERR_INVALID_ARG;
   if (total_q >= INT_MAX || total_kv * mask_elem_bytes >= INT_MAX) return SPD_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < spd_mask_varlen_workspace_bytes(total_q)) return SPD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SPD_ERR_ALIGNMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   const size_t part = round_up(size_t(total_q) * 4, 256);
@@ -229,16 +376,18 @@ extern "C" spd_status spd_mask_to_varlen(const void *mask, int32_t mask_elem_byt
   const int Tq = int(total_q);
   prof_start(SPD_K_MASK_VARLEN, st);
   const int64_t waves_grid = std::min<int64_t>((total_q + 3) / 4, int64_t(device_cu_count()) * 16);
-  hipLaunchKernelGGL(k_row_extent, dim3(unsigned(std::max<int64_t>(1, waves_grid))), dim3(256), 0, st,
-                     static_cast<const unsigned char *>(mask), total_q, int(total_kv * mask_elem_bytes),
-                     int(mask_elem_bytes), first, last);
+  const int64_t row_bytes = total_kv * mask_elem_bytes;
+  if (row_bytes % 16 == 0 && aligned16(mask))
+    hipLaunchKernelGGL(k_row_extent16, dim3(unsigned(std::max<int64_t>(1, waves_grid))), dim3(256), 0, st,
+                       static_cast<const u32x4 *>(mask), total_q, int(row_bytes / 16), int(mask_elem_bytes), first,
+                       last);
+  else
+    hipLaunchKernelGGL(k_row_extent, dim3(unsigned(std::max<int64_t>(1, waves_grid))), dim3(256), 0, st,
+                       static_cast<const unsigned char *>(mask), total_q, int(row_bytes), int(mask_elem_bytes), first,
+                       last);
   SPD_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_mask_owner, dim3(1), dim3(kScan), 0, st, Tq, first, owner);
-  SPD_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_mask_blocks, dim3(1), dim3(kScan), 0, st, Tq, owner, last, cu_seqlens_q, cu_seqlens_k, stats);
-  SPD_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_mask_check, dim3((Tq + 255) / 256), dim3(256), 0, st, Tq, first, last, cu_seqlens_q,
-                     cu_seqlens_k, stats);
+  hipLaunchKernelGGL(k_mask_scan, dim3(1), dim3(kScan), 0, st, Tq, first, last, owner, cu_seqlens_q, cu_seqlens_k,
+                     stats);
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_MASK_VARLEN, st);
   return SPD_OK;

@@ -143,6 +143,7 @@ def test_varlen_calls_reject_bad_arguments():
     assert lib.spd_mask_to_varlen(None, 1, 10, 10, A[11], A[12], A[13], A[14], ws, None) == INVALID
     assert lib.spd_mask_to_varlen(A[10], 1, 10, 10, A[11], A[12], A[13], A[14], ws - 1, None) == WS
     assert lib.spd_mask_to_varlen(A[10], 8, 10, 2**28, A[11], A[12], A[13], A[14], ws, None) == UNSUPPORTED
+    assert lib.spd_mask_to_varlen(A[10], 1, 10, 10, A[11], A[12], A[13], A[14] + 4, ws, None) == ALIGN
     p = _plan()
     assert lib.spd_varlen_params(ctypes.byref(p), None, A[13], A[14], A[15], None) == INVALID
 

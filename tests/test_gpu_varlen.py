@@ -39,14 +39,39 @@ def _check(mask_np, dtype=torch.bool):
 
 @pytest.mark.parametrize("style", ["full", "causal", "bottom_right"])
 @pytest.mark.parametrize("dtype", [torch.bool, torch.int32])
-def test_block_masks(style, dtype):
+@pytest.mark.parametrize("row_align", [1, 16], ids=["any_row_bytes", "row_bytes_16x"])
+def test_block_masks(style, dtype, row_align):
+    """row_bytes_16x pads trailing all-zero key columns so each row is a multiple of 16 bytes (the 16-byte read
+    path); any_row_bytes keeps odd row lengths (the byte path)."""
     rng = np.random.default_rng(51)
-    for n, hi in ((1, 9), (6, 40), (40, 90)):          # the last spans several 1024-row scan chunks
+    esz = torch.tensor([], dtype=dtype).element_size()
+    for n, hi in ((1, 9), (6, 40), (40, 90)):
         k_lens = rng.integers(1, hi, n).tolist()
         q_lens = list(k_lens) if style == "causal" else rng.integers(1, hi, n).tolist()
-        say(f"[varlen] {style} {dtype} blocks={n} rows={sum(q_lens)}")
-        got = _check(_block_mask(q_lens, k_lens, style), dtype)
+        m = _block_mask(q_lens, k_lens, style)
+        if row_align == 16:
+            m = np.pad(m, ((0, 0), (0, (-m.shape[1]) % (16 // esz))))
+        elif (m.shape[1] * esz) % 16 == 0:
+            m = np.pad(m, ((0, 0), (0, 1)))
+        say(f"[varlen] {style} {dtype} blocks={n} rows={sum(q_lens)} cols={m.shape[1]}")
+        got = _check(m, dtype)
         assert got["num_seqs"] == n and got["mismatched_rows"] == 0
+
+
+@pytest.mark.parametrize("style", ["full", "bottom_right"])
+def test_block_masks_many_rows(style):
+    """More rows than one pass of the scans covers (16,384), with blocks and rows that see nothing straddling the
+    pass boundaries."""
+    rng = np.random.default_rng(53)
+    n = 300
+    q_lens = rng.integers(1, 140, n).tolist()
+    k_lens = rng.integers(1, 16, n).tolist()
+    m = _block_mask(q_lens, k_lens, style)
+    say(f"[varlen] many rows: {style} blocks={n} rows={m.shape[0]} cols={m.shape[1]}")
+    assert m.shape[0] > 16384
+    got = _check(m)
+    assert got["num_seqs"] == n and got["mismatched_rows"] == 0
+    _check(np.pad(m, ((0, 0), (0, (-m.shape[1]) % 16))))
 
 
 def test_malformed_and_empty_masks():
