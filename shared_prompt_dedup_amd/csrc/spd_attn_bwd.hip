@@ -42,34 +42,54 @@ constexpr int kDkdvKeys = 256;  // keys per k_dkdv tile (8 waves x 32)
 // D and Ls have a row stride of Tp >= T + 64 so that 64-row blocks starting
 // below T never leave them; the padding rows are set to 0 and every reader
 // masks them.
+// One block per (32-row chunk, group of HG heads): the block reads its rows'
+// HG heads as contiguous runs of (row, head) pairs, stages the sums in LDS and
+// writes each head's 32 rows of D and Ls as one 128-byte line, so no line is
+// shared between blocks that may run on different XCDs.
 template <int D>
-__global__ void __launch_bounds__(256) k_bwd_pre(int64_t rows_x_heads, int Hq, int T, int Tp, float inv_scale,
+__global__ void __launch_bounds__(256) k_bwd_pre(int Hq, int HG, int T, int Tp, float inv_scale,
                                                  const __bf16 *__restrict__ o, const __bf16 *__restrict__ dout,
                                                  const float *__restrict__ lse, spd_plan plan,
                                                  float *__restrict__ Dbuf, float *__restrict__ Lbuf,
                                                  int *__restrict__ send) {
-  constexpr int LPR = D / 8;     // lanes per (row, head)
-  constexpr int RPW = 64 / LPR;  // (row, head) pairs per wave
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-  const int64_t i = wave * RPW + lane / LPR;
-  const int sub = lane % LPR;
-  float s = 0.0f;
-  if (i < rows_x_heads) {
-    const bf16x8 a = ld_global8(o + i * D + sub * 8);
-    const bf16x8 b = ld_global8(dout + i * D + sub * 8);
+  constexpr int LPR = D / 8;              // lanes per (row, head)
+  constexpr int PPP = 256 / LPR;          // (row, head) pairs per pass of the block
+  constexpr int R = 32;                   // rows per block
+  __shared__ float sD[16 * R];
+  const int ngrp = Hq / HG;
+  const int h0 = (blockIdx.x % ngrp) * HG;
+  const int r0 = (blockIdx.x / ngrp) * R;
+  const int sub = threadIdx.x % LPR;
+  for (int p0 = 0; p0 < R * HG; p0 += PPP) {
+    const int p = p0 + threadIdx.x / LPR;      // pair: row r0 + p / HG, head h0 + p % HG
+    const int row = r0 + p / HG, hh = p % HG;
+    float s = 0.0f;
+    if (row < T) {
+      const int64_t off = (int64_t(row) * Hq + h0 + hh) * D + sub * 8;
+      const bf16x8 a = ld_global8(o + off);
+      const bf16x8 b = ld_global8(dout + off);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s = fmaf(static_cast<float>(a[e]), static_cast<float>(b[e]), s);
+      for (int e = 0; e < 8; ++e) s = fmaf(static_cast<float>(a[e]), static_cast<float>(b[e]), s);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (sub == 0) sD[hh * R + p / HG] = -s;
   }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (i < rows_x_heads && sub == 0) {
-    const int64_t row = i / Hq;
-    const int h = static_cast<int>(i % Hq);
-    const int64_t at = int64_t(h) * Tp + row;
-    Dbuf[at] = -s;
-    Lbuf[at] = -lse[int64_t(h) * T + row] * inv_scale;
-    if (h == 0) {
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < HG * R; idx += blockDim.x) {
+    const int hh = idx / R, row = r0 + idx % R;
+    const int64_t at = int64_t(h0 + hh) * Tp + row;
+    if (row < T) {
+      Dbuf[at] = sD[idx];
+      Lbuf[at] = -lse[int64_t(h0 + hh) * T + row] * inv_scale;
+    } else if (row < Tp) {       // padding rows [T, Tp) read as zeros
+      Dbuf[at] = 0.0f;
+      Lbuf[at] = 0.0f;
+    }
+  }
+  if (h0 == 0 && threadIdx.x < R) {
+    const int row = r0 + static_cast<int>(threadIdx.x);
+    if (row < T) {
       const int src = plan.src[row];
       const int b = static_cast<int>(src / plan.S);
       const int64_t t = src - int64_t(b) * plan.S;
@@ -84,15 +104,6 @@ __global__ void __launch_bounds__(256) k_bwd_pre(int64_t rows_x_heads, int Hq, i
       }
       send[row] = end;
     }
-  }
-  // zero the padding rows [T, Tp) of D and Ls
-  const int64_t pad = int64_t(Tp - T) * Hq;
-  const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t nthreads = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t j = tid; j < pad; j += nthreads) {
-    const int64_t a = j / (Tp - T), r = T + j % (Tp - T);
-    Dbuf[a * Tp + r] = 0.0f;
-    Lbuf[a * Tp + r] = 0.0f;
   }
 }
 
@@ -527,16 +538,16 @@ spd_status attn_bwd_bf16(const spd_attn_desc &d, const spd_plan &plan, int64_t T
   const auto *vv = static_cast<const __bf16 *>(v);
   const auto *oo = static_cast<const __bf16 *>(o);
   const auto *dd = static_cast<const __bf16 *>(dout);
-  const int64_t n = T * d.num_q_heads;
-  const int rpw = 64 / (d.head_dim / 8);
-  const int64_t waves = (n + rpw - 1) / rpw;
-  const dim3 gpre(static_cast<unsigned>((waves + 3) / 4));
+  int hg = 16;                              // heads per block: the largest divisor of Hq up to 16
+  while (d.num_q_heads % hg) --hg;
+  // blocks cover rows [0, Tp): the padding rows are written as zeros
+  const dim3 gpre(static_cast<unsigned>((Tp + 31) / 32 * (d.num_q_heads / hg)));
   prof_start(SPD_K_BWD_PRE, st);
   if (d.head_dim == 128)
-    hipLaunchKernelGGL(k_bwd_pre<128>, gpre, dim3(256), 0, st, n, d.num_q_heads, int(T), int(Tp),
+    hipLaunchKernelGGL(k_bwd_pre<128>, gpre, dim3(256), 0, st, d.num_q_heads, hg, int(T), int(Tp),
                        1.0f / d.softmax_scale, oo, dd, lse, plan, Dbuf, Lbuf, send);
   else
-    hipLaunchKernelGGL(k_bwd_pre<64>, gpre, dim3(256), 0, st, n, d.num_q_heads, int(T), int(Tp),
+    hipLaunchKernelGGL(k_bwd_pre<64>, gpre, dim3(256), 0, st, d.num_q_heads, hg, int(T), int(Tp),
                        1.0f / d.softmax_scale, oo, dd, lse, plan, Dbuf, Lbuf, send);
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_BWD_PRE, st);
