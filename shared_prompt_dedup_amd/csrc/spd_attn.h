@@ -69,18 +69,30 @@ inline int64_t tile_capacity(int64_t B, int64_t T, int rows_per_tile) {
   return (T + rows_per_tile - 1) / rows_per_tile + 2 * B + 2;
 }
 
-// Builds a tile list on the device (one block), sorted by decreasing cost so
-// that the heaviest tiles are dispatched first.  `tmp` and `out` hold
+// One tile list to build on the device (one block), sorted by decreasing cost
+// so that the heaviest tiles are dispatched first.  `tmp` and `out` hold
 // `cap` tiles, `goff` B + 1 ints of scratch; *n_out receives the count.
 // Key tiles may be split (see Tile) when `splits` is given: its groups are
 // written there, and the arrival counters of each (group, kv head) in
 // `arrivals` are cleared; `cap` then includes `max_slots` tiles of room for
 // the extra chunks; `blocks_per_tile` (kv heads) and `n_cu` size a CU's fair
 // share.
-spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, int *goff,
-                              Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st,
-                              SplitGroup *splits = nullptr, int *arrivals = nullptr, int max_slots = 0,
-                              int blocks_per_tile = 1, int n_cu = 0);
+struct TileJob {
+  int rows_per_tile = 0;
+  int mode = kQueryTiles;
+  int cap = 0;
+  int *goff = nullptr;
+  Tile *tmp = nullptr, *out = nullptr;
+  int *n_out = nullptr;
+  SplitGroup *splits = nullptr;
+  int *arrivals = nullptr;
+  int max_slots = 0, blocks_per_tile = 1, n_cu = 0;
+};
+
+// Builds `job`'s list, and `second`'s in the same launch when given (the two
+// must not share scratch).
+spd_status launch_build_tiles(const spd_plan &plan, int64_t T, const TileJob &job, hipStream_t st,
+                              const TileJob *second = nullptr);
 
 // fp32 correctness kernels (plain arithmetic, one row per thread).
 spd_status attn_fwd_f32(const spd_attn_desc &d, const spd_plan &plan, int64_t T, const Tile *tiles,

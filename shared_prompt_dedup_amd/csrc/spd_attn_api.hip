@@ -55,12 +55,14 @@ __device__ inline int chunks_of(const Tile &t, int limit, int *rows) {
 // One block: per-group tile counts and their exclusive scan (goff[0..G]),
 // then one thread per tile (its group found by binary search over goff),
 // then a counting sort by decreasing cost.
-__global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int T, int TM, int mode, int cap,
-                                                               int *__restrict__ goff, Tile *__restrict__ tmp,
-                                                               Tile *__restrict__ out, int *__restrict__ n_out,
-                                                               SplitGroup *__restrict__ splits,
-                                                               int *__restrict__ arrivals, int max_slots,
-                                                               int blocks_per_tile, int n_cu) {
+__device__ void build_tiles(const spd_plan &plan, int T, const TileJob &job) {
+  const int TM = job.rows_per_tile, mode = job.mode, cap = job.cap;
+  int *__restrict__ goff = job.goff;
+  Tile *__restrict__ tmp = job.tmp;
+  Tile *__restrict__ out = job.out;
+  SplitGroup *__restrict__ splits = job.splits;
+  int *__restrict__ arrivals = job.arrivals;
+  const int max_slots = job.max_slots, blocks_per_tile = job.blocks_per_tile, n_cu = job.n_cu;
   __shared__ int scan_tmp[kPlanThreads / 64];
   __shared__ int hist[kBuckets];
   const int tid = threadIdx.x;
@@ -266,25 +268,29 @@ __global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int
     const int bkt = kBuckets - 1 - min(t.cost >> shift, kBuckets - 1);
     out[atomicAdd(&hist[bkt], 1)] = t;
   }
-  if (tid == 0) *n_out = M;
+  if (tid == 0) *job.n_out = M;
+}
+
+// Block b builds job b's list.
+__global__ void __launch_bounds__(kPlanThreads) k_build_tiles(spd_plan plan, int T, TileJob j0, TileJob j1) {
+  build_tiles(plan, T, blockIdx.x == 0 ? j0 : j1);
 }
 
 }  // namespace
 
-spd_status launch_build_tiles(const spd_plan &plan, int64_t T, int rows_per_tile, TileMode mode, int *goff,
-                              Tile *tmp, Tile *out, int *n_out, int64_t cap, hipStream_t st, SplitGroup *splits,
-                              int *arrivals, int max_slots, int blocks_per_tile, int n_cu) {
+spd_status launch_build_tiles(const spd_plan &plan, int64_t T, const TileJob &job, hipStream_t st,
+                              const TileJob *second) {
   static_assert(kBuckets == 4 * kPlanThreads, "bucket scan assumes 4 buckets per thread");
-  hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(kPlanThreads), 0, st, plan, int(T), rows_per_tile, int(mode),
-                     int(cap), goff, tmp, out, n_out, splits, arrivals, max_slots, blocks_per_tile, n_cu);
+  hipLaunchKernelGGL(k_build_tiles, dim3(second ? 2 : 1), dim3(kPlanThreads), 0, st, plan, int(T), job,
+                     second ? *second : job);
   return check_launch();
 }
 
 namespace {
 
 struct AttnWs {
-  Tile *qtiles = nullptr, *ktiles = nullptr, *tmp = nullptr;
-  int *counts = nullptr, *goff = nullptr;
+  Tile *qtiles = nullptr, *ktiles = nullptr, *tmp = nullptr, *tmp2 = nullptr;
+  int *counts = nullptr, *goff = nullptr, *goff2 = nullptr;
   float *Dbuf = nullptr, *L2buf = nullptr;
   int *segp = nullptr;
   SplitGroup *splits = nullptr;
@@ -300,7 +306,7 @@ int dq_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dq_
 int k_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dkdv_bf16_rows_per_tile(d); }
 
 // Workspace: [-D: Hq*Tp floats][-lse/scale: Hq*Tp floats][segment ends: Tp ints]
-//            [query tiles][key tiles][scratch tiles][counts][group offsets]
+//            [query tiles][key tiles][scratch tiles x 2][counts][group offsets x 2]
 //            bf16 only: [split groups][arrival counters: slots x Hkv ints]
 //                       [partial dK][partial dV] (slots x Hkv x 256 x D floats each)
 AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
@@ -329,9 +335,13 @@ AttnWs carve(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
   off += kb;
   if (p) w.tmp = reinterpret_cast<Tile *>(p + off);
   off += tb;
+  if (p) w.tmp2 = reinterpret_cast<Tile *>(p + off);
+  off += tb;
   if (p) w.counts = reinterpret_cast<int *>(p + off);
   off += 256;
   if (p) w.goff = reinterpret_cast<int *>(p + off);
+  off += round_up(size_t(B + 1) * 4, 256);
+  if (p) w.goff2 = reinterpret_cast<int *>(p + off);
   off += round_up(size_t(B + 1) * 4, 256);
   if (w.slots) {
     const size_t pb = size_t(w.slots) * size_t(d.num_kv_heads) * size_t(k_rows(d)) * size_t(d.head_dim) * 4;
@@ -386,7 +396,15 @@ extern "C" spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_pl
   if (T == 0) return SPD_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnWs w = carve(*desc, plan->B, T, workspace);
-  SPD_TRY(launch_build_tiles(*plan, T, q_rows(*desc), kQueryTiles, w.goff, w.tmp, w.qtiles, w.counts, w.capq, st));
+  TileJob qj;
+  qj.rows_per_tile = q_rows(*desc);
+  qj.mode = kQueryTiles;
+  qj.cap = int(w.capq);
+  qj.goff = w.goff;
+  qj.tmp = w.tmp;
+  qj.out = w.qtiles;
+  qj.n_out = w.counts;
+  SPD_TRY(launch_build_tiles(*plan, T, qj, st));
   if (desc->dtype == SPD_F32)
     return attn_fwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, static_cast<const float *>(q),
                         static_cast<const float *>(k), static_cast<const float *>(v), static_cast<float *>(o), lse,
@@ -406,9 +424,29 @@ extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_pl
   if (T == 0) return SPD_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnWs w = carve(*desc, plan->B, T, workspace);
-  SPD_TRY(launch_build_tiles(*plan, T, dq_rows(*desc), kQueryTiles, w.goff, w.tmp, w.qtiles, w.counts, w.capq, st));
-  SPD_TRY(launch_build_tiles(*plan, T, k_rows(*desc), kKeyTiles, w.goff, w.tmp, w.ktiles, w.counts + 1, w.capk, st,
-                             w.splits, w.arrivals, w.slots, desc->num_kv_heads, device_cu_count()));
+  // both lists in one launch, one block each
+  TileJob qj;
+  qj.rows_per_tile = dq_rows(*desc);
+  qj.mode = kQueryTiles;
+  qj.cap = int(w.capq);
+  qj.goff = w.goff;
+  qj.tmp = w.tmp;
+  qj.out = w.qtiles;
+  qj.n_out = w.counts;
+  TileJob kj;
+  kj.rows_per_tile = k_rows(*desc);
+  kj.mode = kKeyTiles;
+  kj.cap = int(w.capk);
+  kj.goff = w.goff2;
+  kj.tmp = w.tmp2;
+  kj.out = w.ktiles;
+  kj.n_out = w.counts + 1;
+  kj.splits = w.splits;
+  kj.arrivals = w.arrivals;
+  kj.max_slots = w.slots;
+  kj.blocks_per_tile = desc->num_kv_heads;
+  kj.n_cu = device_cu_count();
+  SPD_TRY(launch_build_tiles(*plan, T, qj, st, &kj));
   if (desc->dtype == SPD_F32)
     return attn_bwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, w.ktiles, w.counts + 1, w.capk,
                         static_cast<const float *>(q), static_cast<const float *>(k), static_cast<const float *>(v),
