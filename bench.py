@@ -48,10 +48,10 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "b12cd298fb0d4953c7d5b55014384cb3129f0a80349084c488d456a163fa9174"
+TRAFFIC_SOURCES_SHA256 = "858ae2c997f690c7e4668e733fc0d5c1d36e0066d88f3417223ccb4f133261d6"
 TRAFFIC_KIB = {   # kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
-    "fwd": (220239, 99911), "bwd_pre": (104874, 25354), "bwd_dq": (271375, 98344), "bwd_dkdv": (686735, 98558),
-    "reconstruct": (49569, 557505), "pack_rows": (49553, 98336),
+    "fwd": (220393, 99951), "bwd_pre": (99147, 3176), "bwd_dq": (271455, 98377), "bwd_dkdv": (682579, 98819),
+    "reconstruct": (49569, 557432), "pack_rows": (49553, 98338),
 }
 
 

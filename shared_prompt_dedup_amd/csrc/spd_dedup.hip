@@ -310,6 +310,48 @@ __device__ inline void for_kept_columns(const void *mask, int esz, int unpad, in
 // One block per sample: dst for every (b, t); src, seg_start, dedup ids and
 // positions for the packed rows this sample owns (its response, and its
 // group's prompt when it is the first member).
+// Padded format (every column kept): a column's packed row is its offset in
+// its segment, so one thread per batch cell, no scan.  Same results as
+// k_scatter with unpad = 0.
+__global__ void __launch_bounds__(256) k_scatter_dense(int64_t S, int64_t P, const int64_t *__restrict__ ids,
+                                                        const int64_t *__restrict__ pos, const void *mask, int esz,
+                                                        spd_plan plan, int64_t *__restrict__ dids,
+                                                        int64_t *__restrict__ dpos) {
+  const int64_t cells = plan.B * S;
+  const int64_t L0 = plan.counts[4];
+  int kept_pads = 0;
+  for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < cells; c += int64_t(gridDim.x) * blockDim.x) {
+    const int b = static_cast<int>(c / S);
+    const int64_t t = c - int64_t(b) * S;
+    int j, from, seg;
+    if (t < L0) {                 // shared prefix: packed from the first group's first sample
+      from = plan.rep[0];
+      j = static_cast<int>(t);
+      seg = 0;
+    } else if (t < P) {           // the group's prompt, from its first member
+      const int g = plan.group_of[b];
+      from = plan.rep[g];
+      seg = plan.prompt_off[g];
+      j = seg + static_cast<int>(t - L0);
+    } else {                      // the sample's own response
+      from = b;
+      seg = plan.resp_off[b];
+      j = seg + static_cast<int>(t - P);
+    }
+    plan.dst[c] = j;
+    if (b == from) {
+      plan.src[j] = static_cast<int32_t>(c);
+      plan.seg_start[j] = seg;
+      dids[j] = ids[c];
+      dpos[j] = pos[c];
+      if (mask) kept_pads += !mask_at(mask, esz, c);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) kept_pads += __shfl_xor(kept_pads, off, 64);
+  if (__lane_id() == 0 && kept_pads) atomicAdd(&plan.counts[3], kept_pads);
+}
+
 __global__ void __launch_bounds__(256) k_scatter(int64_t S, int64_t P, const int64_t *__restrict__ ids,
                                                   const int64_t *__restrict__ pos, const void *mask, int esz,
                                                   int unpad, spd_plan plan, int64_t *__restrict__ dids,
@@ -688,8 +730,12 @@ extern "C" spd_status spd_pack(const int64_t *input_ids, const int64_t *position
   SPD_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_seg_offsets, dim3(1), dim3(kFinalThreads), 0, st, int(B), seg, *plan);
   SPD_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_scatter, dim3(B), dim3(256), 0, st, S, P, input_ids, position_ids, attention_mask, esz,
-                     use_unpad, *plan, dedup_ids, dedup_pos);
+  if (use_unpad)
+    hipLaunchKernelGGL(k_scatter, dim3(B), dim3(256), 0, st, S, P, input_ids, position_ids, attention_mask, esz,
+                       use_unpad, *plan, dedup_ids, dedup_pos);
+  else
+    hipLaunchKernelGGL(k_scatter_dense, dim3(unsigned(std::min<int64_t>((B * S + 255) / 256, 65536))), dim3(256),
+                       0, st, S, P, input_ids, position_ids, attention_mask, esz, *plan, dedup_ids, dedup_pos);
   SPD_LAUNCH_CHECK();
   return SPD_OK;
 }
