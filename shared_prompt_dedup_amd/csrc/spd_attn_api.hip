@@ -145,9 +145,9 @@ __device__ void build_tiles(const spd_plan &plan, int T, const TileJob &job) {
   __syncthreads();
   // When the heaviest key tile is about a CU's fair share of the blocks'
   // reader rows or more, the in-order dispatch cannot even the CUs out: tiles
-  // above half that share are cut into chunks, the limit growing until the
-  // chunks fit the partial-sum slots.  Below that, splitting only adds the
-  // partial sums' traffic.
+  // above a limit are cut into chunks, the limit growing until the chunks fit
+  // the partial-sum slots.  Below that, splitting only adds the partial sums'
+  // traffic.
   int limit = INT_MAX;
   if (splits && n_cu > 0 && max_slots >= 2) {
     __shared__ long long red[kPlanThreads / 64];
@@ -174,7 +174,11 @@ __device__ void build_tiles(const spd_plan &plan, int T, const TileJob &job) {
       mx = max(mx, redmax[w]);
     }
     const long long share = tot * blocks_per_tile / n_cu;
-    long long lim = 10LL * mx >= 9LL * share ? share / 2 : LLONG_MAX;
+    // chunks of half a share; of two thirds when the heaviest tile holds 1.4 to
+    // 3 shares (fewer, larger chunks pack better there: dispatch model of the
+    // planner's tile costs over the CUs)
+    long long lim = LLONG_MAX;
+    if (10LL * mx >= 9LL * share) lim = (10LL * mx >= 14LL * share && mx < 3LL * share) ? share * 2 / 3 : share / 2;
     lim = lim < 2048 ? 2048 : lim;
     for (int attempt = 0; attempt < 12; ++attempt) {
       int need = 0;
