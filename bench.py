@@ -48,10 +48,10 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "858ae2c997f690c7e4668e733fc0d5c1d36e0066d88f3417223ccb4f133261d6"
+TRAFFIC_SOURCES_SHA256 = "927fe1e179a76a34473b7e4c48e40ea543d9bb470cce9be7742e977b1fec614d"
 TRAFFIC_KIB = {   # kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
-    "fwd": (220393, 99951), "bwd_pre": (99147, 3176), "bwd_dq": (271455, 98377), "bwd_dkdv": (682579, 98819),
-    "reconstruct": (49569, 557432), "pack_rows": (49553, 98338),
+    "fwd": (220413, 99911), "bwd_pre": (99147, 3176), "bwd_dq": (271453, 98350), "bwd_dkdv": (692246, 98846),
+    "reconstruct": (49569, 557462), "pack_rows": (49553, 98332),
 }
 
 
