@@ -40,6 +40,10 @@ SMALL = {
                               resp_len_range=(1, 40), seed=35),
     "bf16_gqa8_d64": _base.scaled(name="bf16_gqa8_d64", num_prompts=2, rollout_n=2, prompt_len=90, response_len=33,
                                   num_q_heads=8, num_kv_heads=1, head_dim=64, dtype="bf16", sigma=0.5, seed=36),
+    # one kv head read by 16 query heads: four query heads per block, the most partial-sum slots
+    "bf16_mqa16": _base.scaled(name="bf16_mqa16", num_prompts=2, rollout_n=2, prompt_len=330, response_len=90,
+                               num_q_heads=16, num_kv_heads=1, head_dim=128, dtype="bf16", sigma=0.5,
+                               resp_len_range=(5, 90), seed=43),
     "bf16_gqa3": _base.scaled(name="bf16_gqa3", num_prompts=2, rollout_n=2, prompt_len=70, response_len=30,
                               num_q_heads=3, num_kv_heads=1, head_dim=128, dtype="bf16", sigma=0.5, seed=37),
     # mid-size, every element compared: 2 prompts x 4 responses, prompt 2048, response 512, GQA 16/8/128

@@ -38,7 +38,7 @@ def _check(mask_np, dtype=torch.bool):
 
 
 @pytest.mark.parametrize("style", ["full", "causal", "bottom_right"])
-@pytest.mark.parametrize("dtype", [torch.bool, torch.int32])
+@pytest.mark.parametrize("dtype", [torch.bool, torch.int32, torch.int64])
 @pytest.mark.parametrize("row_align", [1, 16], ids=["any_row_bytes", "row_bytes_16x"])
 def test_block_masks(style, dtype, row_align):
     """row_bytes_16x pads trailing all-zero key columns so each row is a multiple of 16 bytes (the 16-byte read
@@ -50,7 +50,7 @@ def test_block_masks(style, dtype, row_align):
         q_lens = list(k_lens) if style == "causal" else rng.integers(1, hi, n).tolist()
         m = _block_mask(q_lens, k_lens, style)
         if row_align == 16:
-            m = np.pad(m, ((0, 0), (0, (-m.shape[1]) % (16 // esz))))
+            m = np.pad(m, ((0, 0), (0, (-m.shape[1]) % max(1, 16 // esz))))
         elif (m.shape[1] * esz) % 16 == 0:
             m = np.pad(m, ((0, 0), (0, 1)))
         say(f"[varlen] {style} {dtype} blocks={n} rows={sum(q_lens)} cols={m.shape[1]}")
