@@ -308,7 +308,14 @@ typedef struct spd_attn_desc {
   float softmax_scale;   /* usually 1 / sqrt(d); must be > 0 */
 } spd_attn_desc;
 
-/* Workspace bytes the attention calls need for T packed rows of a B-sample plan. */
+/*
+ * Workspace bytes the attention calls need for T packed rows of a B-sample
+ * plan (the same query serves the forward and the backward).  For bf16 it
+ * includes the backward's partial-sum slots for split key tiles:
+ * min(64, 1024 / Hkv) slots of 256 keys x Hkv x d fp32, for dk and for dv
+ * (128 MiB at Hkv 8, d 128; at most 256 MiB); the forward never touches them.
+ * Returns 0 for an invalid descriptor, B < 1 or T < 0.
+ */
 size_t spd_attn_workspace_bytes(const spd_attn_desc *desc, int64_t B, int64_t T);
 
 /*
