@@ -124,7 +124,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None, help="workload name in workloads.WORKLOADS")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
-    ap.add_argument("--profile-steps", type=int, default=5, help="steps timed per kernel with HIP events")
+    ap.add_argument("--profile-steps", type=int, default=20, help="steps timed per kernel with HIP events")
     ap.add_argument("--share-prefix", action="store_true",
                     help="also pack the prompts' common prefix once (prefix caching); try it with --workload "
                          "prefix_4x8_s4096_p5120_r512")
@@ -227,13 +227,19 @@ def main():
     bwd_flops = 10 * d * Hq * pairs
     value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
 
-    # Per-kernel HIP events (recorded by the library on the launch stream).
-    spd.profile_begin()
+    # Per-kernel HIP events (recorded by the library on the launch stream), one
+    # window per step so that the spread across steps is seen too.
+    per_step = {}
     for _ in range(args.profile_steps):
+        spd.profile_begin()
         step()
-    torch.cuda.synchronize()
-    prof = spd.profile_end()
-    kern_ms = {kname: (tot / n if n else None) for kname, (n, tot) in prof.items()}
+        torch.cuda.synchronize()
+        for kname, (n, tot) in spd.profile_end().items():
+            if n:
+                per_step.setdefault(kname, []).append(tot / n)
+    kern_ms = {kname: float(np.mean(v)) for kname, v in per_step.items()}
+    kern_spread = {kname: [round(float(x), 4) for x in np.percentile(v, [10, 50, 90])]
+                   for kname, v in per_step.items()}
     row_bytes = W * 2
     Ta = {"split": T, "standard": None, "padded_mask": None}[args.mode]     # rows the attention kernels run on
     if args.mode == "standard":
@@ -263,6 +269,30 @@ def main():
             ach = work / (ms * 1e-3) / 1e9
             kernels[kname] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+        kernels[kname]["ms_p10_p50_p90"] = kern_spread[kname]
+    # The gathers again, alone, with the 256 MB Infinity Cache flushed before each
+    # call by reading a 512 MB buffer (a read leaves clean lines behind, so the
+    # flush adds no write-back to the timed call; outside the timed windows).
+    if args.mode == "split":
+        flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+        o_rows = torch.empty(T, W, dtype=torch.bfloat16, device=dev)
+        for kname, call in (("reconstruct", lambda: spd.reconstruct(o_rows, info)),
+                            ("pack_rows", lambda: spd.pack_rows(hidden, info))):
+            times = []
+            for _ in range(max(5, args.profile_steps)):
+                flush.sum()
+                torch.cuda.synchronize()
+                spd.profile_begin()
+                call()
+                torch.cuda.synchronize()
+                n, tot = spd.profile_end()[kname]
+                times.append(tot / n)
+            ms = float(np.median(times))
+            ach = kernel_work[kname][1] / (ms * 1e-3) / 1e9
+            kernels[kname + "_cache_flushed"] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1),
+                                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                                 "frac": round(ach / PEAK_HBM_GBS, 4)}
+        del flush, o_rows
     # Flash Attention Integration: the block-diagonal prompt-to-prompt mask of this batch -> cu_seqlens.
     if args.mode == "split":
         G = info["G"]
