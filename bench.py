@@ -85,6 +85,19 @@ def attended_pairs(info):
     return pairs
 
 
+def attention_split(kern_ms, fwd_flops, bwd_flops):
+    """Forward, backward and forward + backward kernel time and useful TFLOP/s (backward = preprocessing, dq and
+    dk/dv, FlashAttention's 10 d FLOPs per pair and head)."""
+    fwd = kern_ms.get("fwd")
+    bwd = sum(kern_ms.get(k) or 0.0 for k in ("bwd_pre", "bwd_dq", "bwd_dkdv")) or None
+    out = {}
+    for key, ms, flops in (("fwd", fwd, fwd_flops), ("bwd", bwd, bwd_flops),
+                           ("fwd_bwd", (fwd or 0.0) + (bwd or 0.0) or None, fwd_flops + bwd_flops)):
+        if ms:
+            out[key] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    return out
+
+
 def cpu_baseline(w, bt, pairs_per_head, min_seconds=10.0):
     """The oracle, as it stands, forward + backward (fp64) on query heads of the same
     workload, one head at a time until at least `min_seconds` of CPU work."""
@@ -351,6 +364,7 @@ def main():
                    "attention": args.mode, "shared_prefix_rows": int(info.get("prefix_len", 0))},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "attention_kernels_tflops": round((fwd_flops + bwd_flops) / (attn_ms * 1e-3) / 1e12, 2),
+        "attention_split": attention_split(kern_ms, fwd_flops, bwd_flops),
         "roofline": roof,
         "kernels": kernels,
         "hbm_copy_gbs": round(copy_gbs, 1),
