@@ -108,7 +108,7 @@ __device__ inline int swz_off(int row, int chunk) {
 // inline assembly: the compiler, seeing an LDS DMA, would otherwise make every
 // later transposing LDS read wait for all outstanding vector loads, including
 // the prefetches of later stages.  Callers wait for completion themselves
-// (wait_ring, wait_tile) before a barrier publishes the data.  The s_nop is the
+// (wait_ring) before a barrier publishes the data.  The s_nop is the
 // wait state an LDS DMA needs after M0 is written.
 __device__ inline void dma16(const void *base, unsigned voff, const char *lds) {
   const unsigned m = __builtin_amdgcn_readfirstlane(
@@ -166,13 +166,6 @@ __device__ inline void dma_rows2(char *tile, const __bf16 *src, int x0, int lenV
     const int row = min(x < lenV ? v0 + x : u0 + (x - lenV), T - 1);
     dma16(base, static_cast<unsigned>(row) * row_bytes + (chunk << 4), tile + blk * 1024);
   }
-}
-
-// Waits for this wave's outstanding memory operations (direct-to-LDS loads
-// included), then for every wave of the block.
-__device__ inline void wait_tile() {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
 }
 
 // s_waitcnt immediate that waits only until at most N vector-memory operations
