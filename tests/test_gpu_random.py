@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 HEADS = [(2, 1, 64), (4, 2, 128), (4, 4, 64), (8, 2, 128), (3, 1, 128), (16, 1, 64), (4, 1, 128)]
-SEEDS = list(range(24))
+SEEDS = list(range(64))
 
 
 def _config(seed):
