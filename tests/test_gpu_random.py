@@ -1,6 +1,7 @@
 """Randomised GPU parity: small batches drawn from a seeded generator -- group
-count, rollouts, prompt and response lengths, padded or unpadded packing, a
-shared prompt prefix or none, GQA ratio, head dimension, bf16 or fp32 -- each
+count, rollouts, prompt and response lengths, padded, unpadded or padded with
+a mask, a shared prompt prefix or none, GQA ratio, head dimension, bf16 or
+fp32; every fourth also in standard (full-batch) mode -- each
 checked end to end against the oracle: plan arrays and packed ids bit-exact,
 row moves bit-exact, attention forward and backward within the per-dtype
 tolerances (the non-deduplicated per-sample definition)."""
@@ -31,33 +32,35 @@ def _config(seed):
         # key read by hundreds of rows and several query heads sums thousands of them
         G, n, P, R = min(G, 2), min(n, 4), min(P, 128), min(R, 64)
         hq, hkv, d = HEADS[int(rng.integers(3))]
-    unpad = bool(rng.random() < 0.5)
+    # packed format: padded without a mask, unpadded, or padded with a mask (pads kept, no part in attention)
+    fmt = ("padded", "unpad", "padded_mask")[int(rng.choice(3, p=[0.35, 0.35, 0.3]))]
     prefix = int(rng.integers(1, P + 1)) if (G >= 2 and rng.random() < 0.35) else 0
     w = WORKLOADS["tiny_fp32"].scaled(
         name=f"random_{seed}", num_prompts=G, rollout_n=n, prompt_len=P, response_len=R, num_q_heads=hq,
         num_kv_heads=hkv, head_dim=d, dtype=dtype, sigma=0.5 if dtype == "bf16" else 1.0,
-        resp_len_range=(0, R) if unpad else None, shared_prefix=prefix, seed=20_000 + seed)
-    return w, prefix > 0
+        resp_len_range=None if fmt == "padded" else (0, R), shared_prefix=prefix, seed=20_000 + seed)
+    return w, fmt, prefix > 0
 
 
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_batch_end_to_end(seed):
     import shared_prompt_dedup_amd as spd
-    w, share = _config(seed)
+    w, fmt, share = _config(seed)
+    unpad = fmt == "unpad"
     say(f"[random {seed}] G={w.num_prompts} n={w.rollout_n} P={w.prompt_len} R={w.response_len} "
-        f"unpad={w.use_unpad} prefix={w.shared_prefix} heads={w.num_q_heads}/{w.num_kv_heads}/{w.head_dim} {w.dtype}")
+        f"{fmt} prefix={w.shared_prefix} heads={w.num_q_heads}/{w.num_kv_heads}/{w.head_dim} {w.dtype}")
     bt = make_batch(w, permute=True)
     groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
     L0 = oracle.find_shared_prefix(bt.input_ids, bt.response_length, groups) if share else 0
     odids, odpos, oinfo = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups,
                                                            uniq, attention_mask=bt.attention_mask,
-                                                           use_unpad=w.use_unpad, prefix_len=L0)
+                                                           use_unpad=unpad, prefix_len=L0)
     ids, pos, mask = (torch.from_numpy(a).cuda() for a in (bt.input_ids, bt.position_ids, bt.attention_mask))
     gg, gu = spd.find_prompt_groups(ids, bt.response_length)
     assert [list(x) for x in gg] == [list(x) for x in groups]
-    gdids, gdpos, ginfo = spd.create_deduplicated_batch(ids, pos, bt.response_length, gg, gu,
-                                                        attention_mask=mask if w.use_unpad else None,
-                                                        use_unpad=w.use_unpad, share_prefix=share)
+    gmask = None if fmt == "padded" else mask
+    gdids, gdpos, ginfo = spd.create_deduplicated_batch(ids, pos, bt.response_length, gg, gu, attention_mask=gmask,
+                                                        use_unpad=unpad, share_prefix=share)
     T = oinfo["T"]
     assert ginfo["T"] == T and ginfo["G"] == oinfo["G"] and ginfo["prefix_len"] == oinfo["prefix_len"]
     np.testing.assert_array_equal(gdids.cpu().numpy(), odids)
@@ -80,13 +83,22 @@ def test_random_batch_end_to_end(seed):
                                   oracle.pack_rows(rows, oinfo))
     if T == 0:
         return
-    # attention, forward and backward
+    # attention, forward and backward; with the padded format and a mask, pad rows are no keys and output 0
+    valid = bt.attention_mask.reshape(-1)[oinfo["src"]] != 0 if fmt == "padded_mask" else None
     xa, q, k, v, do = attn_inputs(w, T)
     o, lse = spd.split_attn_fwd(q, k, v, ginfo)
     dq, dk, dv = spd.split_attn_bwd(q, k, v, o, lse, do, ginfo)
-    ro, rlse = oracle.split_attention_forward(xa.q, xa.k, xa.v, oinfo)
-    rdq, rdk, rdv = oracle.split_attention_backward(xa.q, xa.k, xa.v, xa.do, oinfo)
+    ro, rlse = oracle.split_attention_forward(xa.q, xa.k, xa.v, oinfo, valid=valid)
+    rgrads = oracle.split_attention_backward(xa.q, xa.k, xa.v, xa.do, oinfo, valid=valid)
     compare("o", to_numpy(o), ro, w.dtype)
-    compare("lse", lse.cpu().numpy(), rlse, w.dtype)
-    for key, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+    compare("lse", lse.cpu().numpy(), rlse if valid is None else rlse[:, valid], w.dtype)
+    for key, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), rgrads):
         compare(key, to_numpy(got), ref, w.dtype)
+    if seed % 4 == 0:       # standard mode (attention on the full batch) on the same plan: same function
+        full = spd.create_full_batch(ids, pos, bt.response_length, attention_mask=gmask, use_unpad=unpad)[2]
+        qg, kg, vg = (t.clone().requires_grad_() for t in (q, k, v))
+        so = spd.standard_attention(qg, kg, vg, ginfo, full)
+        so.backward(do)
+        compare("standard o", to_numpy(so.detach()), ro, w.dtype)
+        for key, got, ref in zip(("dq", "dk", "dv"), (qg.grad, kg.grad, vg.grad), rgrads):
+            compare(f"standard {key}", to_numpy(got), ref, w.dtype)
