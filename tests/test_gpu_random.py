@@ -42,10 +42,36 @@ def _config(seed):
     return w, fmt, prefix > 0
 
 
+def _config_medium(seed):
+    """Larger bf16 batches: prompts of hundreds to thousands of tokens, so key tiles are read by more rows than
+    a CU's share and the backward splits them into chunks."""
+    rng = np.random.default_rng(30_000 + seed)
+    G = int(rng.integers(1, 4))
+    n = int(rng.integers(2, 13 // G + 1))
+    P = int(rng.integers(400, 2600))
+    R = int(rng.integers(40, 500))
+    hq, hkv, d = [(2, 1, 128), (4, 2, 64), (4, 1, 128), (2, 2, 128)][int(rng.integers(4))]
+    fmt = ("padded", "unpad", "padded_mask")[seed % 3]
+    prefix = int(rng.integers(1, P)) if (G >= 2 and rng.random() < 0.5) else 0
+    w = WORKLOADS["tiny_fp32"].scaled(
+        name=f"random_medium_{seed}", num_prompts=G, rollout_n=n, prompt_len=P, response_len=R, num_q_heads=hq,
+        num_kv_heads=hkv, head_dim=d, dtype="bf16", sigma=0.5, vocab=151936,
+        resp_len_range=None if fmt == "padded" else (R // 4, R), shared_prefix=prefix, seed=40_000 + seed)
+    return w, fmt, prefix > 0
+
+
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_batch_end_to_end(seed):
+    _end_to_end(seed, *_config(seed))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_medium_batch_end_to_end(seed):
+    _end_to_end(seed, *_config_medium(seed))
+
+
+def _end_to_end(seed, w, fmt, share):
     import shared_prompt_dedup_amd as spd
-    w, fmt, share = _config(seed)
     unpad = fmt == "unpad"
     say(f"[random {seed}] G={w.num_prompts} n={w.rollout_n} P={w.prompt_len} R={w.response_len} "
         f"{fmt} prefix={w.shared_prefix} heads={w.num_q_heads}/{w.num_kv_heads}/{w.head_dim} {w.dtype}")
