@@ -48,10 +48,10 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "927fe1e179a76a34473b7e4c48e40ea543d9bb470cce9be7742e977b1fec614d"
+TRAFFIC_SOURCES_SHA256 = "0e7dae9e454b22f43683bb5200e8f0d3eeae4b56ce6262863e8b20d5bee00f9e"
 TRAFFIC_KIB = {   # kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
-    "fwd": (220413, 99911), "bwd_pre": (99147, 3176), "bwd_dq": (271453, 98350), "bwd_dkdv": (692246, 98846),
-    "reconstruct": (49569, 557462), "pack_rows": (49553, 98332),
+    "fwd": (221740, 99842), "bwd_pre": (99148, 3176), "bwd_dq": (272725, 98307), "bwd_dkdv": (686706, 98685),
+    "reconstruct": (49559, 557491), "pack_rows": (49552, 98330),
 }
 
 
