@@ -62,7 +62,7 @@ class Plan:
         self.src = torch.empty(n, **i32)
         self.dst = torch.empty(n, **i32)
         self.seg_start = torch.empty(n, **i32)
-        self.counts = torch.zeros(8, **i32)
+        self.counts = torch.empty(8, **i32)      # every entry the calls read is written by an earlier call
         self.G: Optional[int] = None
         self.T: Optional[int] = None
         self.use_unpad = False

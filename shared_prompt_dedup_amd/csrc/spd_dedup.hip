@@ -464,7 +464,8 @@ __global__ void __launch_bounds__(kRowThreads) k_pack_rows(int64_t T, int64_t ve
 
 // Packed row j goes to every (b, t) that maps to it: for a prompt row, the
 // same column t of every member of the group (read once, written n times);
-// for a response row, its own (b, t).
+// for a response row, its own (b, t).  Then, when unpad left cells that no
+// packed row maps (counts[2] > 0), those read as zeros.
 __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t S, int64_t P,
                                                               int64_t vec_per_row, spd_plan plan,
                                                               const u32x4 *__restrict__ packed,
@@ -504,6 +505,15 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
           if (c < vec_per_row) stream_store(o + c, v[u]);
         }
       }
+    }
+  }
+  if (plan.counts[2] != 0) {
+    const int64_t cells = plan.B * S;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t r = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; r < cells; r += nwaves) {
+      if (plan.dst[r] >= 0) continue;
+      u32x4 *o = out + r * vec_per_row;
+      for (int64_t c = lane; c < vec_per_row; c += 64) stream_store(o + c, z);
     }
   }
 }
@@ -659,22 +669,6 @@ __global__ void k_singleton_groups(int B, spd_plan plan) {
   }
 }
 
-// Zeros every output row that no packed token maps to (dst == -1).
-__global__ void __launch_bounds__(kRowThreads) k_zero_unmapped(int64_t rows, int64_t vec_per_row,
-                                                                const int32_t *__restrict__ dst,
-                                                                const int32_t *__restrict__ counts,
-                                                                u32x4 *__restrict__ out) {
-  if (counts[2] == 0) return;
-  const int lane = __lane_id();
-  const int64_t nwaves = int64_t(gridDim.x) * (kRowThreads / 64);
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int64_t r = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; r < rows; r += nwaves) {
-    if (dst[r] >= 0) continue;
-    u32x4 *o = out + r * vec_per_row;
-    for (int64_t c = lane; c < vec_per_row; c += 64) stream_store(o + c, z);
-  }
-}
-
 int row_grid(int64_t rows) {
   const int64_t waves_per_block = kRowThreads / 64;
   const int64_t want = (rows + waves_per_block - 1) / waves_per_block;
@@ -792,14 +786,8 @@ extern "C" spd_status spd_reconstruct(const spd_plan *plan, int64_t T, const voi
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t vpr = row_bytes / 16;
   prof_start(SPD_K_RECONSTRUCT, st);
-  if (T > 0) {
-    hipLaunchKernelGGL(k_reconstruct, dim3(row_grid(T)), dim3(kRowThreads), 0, st, T, plan->S, plan->P, vpr,
-                       *plan, static_cast<const u32x4 *>(packed), static_cast<u32x4 *>(out));
-    SPD_LAUNCH_CHECK();
-  }
-  const int64_t rows = plan->B * plan->S;
-  hipLaunchKernelGGL(k_zero_unmapped, dim3(row_grid(rows)), dim3(kRowThreads), 0, st, rows, vpr, plan->dst,
-                     plan->counts, static_cast<u32x4 *>(out));
+  hipLaunchKernelGGL(k_reconstruct, dim3(row_grid(plan->B * plan->S)), dim3(kRowThreads), 0, st, T, plan->S,
+                     plan->P, vpr, *plan, static_cast<const u32x4 *>(packed), static_cast<u32x4 *>(out));
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_RECONSTRUCT, st);
   return SPD_OK;
