@@ -59,44 +59,89 @@ __device__ inline uint64_t mix64(uint64_t z) {
   return z ^ (z >> 31);
 }
 
-// One block per row: an order-dependent hash of the row's P prompt ids, the
-// wrapping sum of mix64(id + position * golden-ratio constant).  It only
-// narrows the candidates; equality is always decided by full comparison.
-__global__ void __launch_bounds__(256) k_hash_rows(const int64_t *__restrict__ ids, int64_t S, int64_t P,
-                                                    uint64_t *__restrict__ hash) {
-  const int64_t b = blockIdx.x;
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
+
+// Prompt tokens hashed by one block of k_hash_rows.
+constexpr int kHashChunk = 2048;
+
+__device__ inline uint64_t token_term(int64_t id, int64_t t) {
+  return mix64(static_cast<uint64_t>(id) + static_cast<uint64_t>(t + 1) * 0x9E3779B97F4A7C15ull);
+}
+
+// A row's hash is an order-dependent function of its P prompt ids: the
+// wrapping sum over tokens t of mix64(id_t + (t + 1) * golden-ratio constant).
+// It only narrows the candidates; equality is always decided by full
+// comparison.  One block per (row, chunk of kHashChunk tokens) writes the
+// chunk's part of the sum to part[row * nch + chunk]; a wrapping sum does not
+// depend on the order its parts are added in.  VEC: rows start on 16-byte
+// boundaries (S even), so token pairs (t, t + 1), t even, load as 16 bytes.
+template <bool VEC>
+__global__ void __launch_bounds__(256) k_hash_rows(const int64_t *__restrict__ ids, int64_t S, int64_t P, int nch,
+                                                    uint64_t *__restrict__ part) {
+  const int64_t b = blockIdx.x / nch;
+  const int64_t t0 = int64_t(blockIdx.x % nch) * kHashChunk;
+  const int64_t t1 = t0 + kHashChunk < P ? t0 + kHashChunk : P;
   const int64_t *row = ids + b * S;
   uint64_t h = 0;
-  for (int64_t t = threadIdx.x; t < P; t += blockDim.x)
-    h += mix64(static_cast<uint64_t>(row[t]) + static_cast<uint64_t>(t + 1) * 0x9E3779B97F4A7C15ull);
-  __shared__ uint64_t part[4];
+  if (VEC) {
+#pragma unroll 4
+    for (int64_t t = t0 + 2 * int64_t(threadIdx.x); t < t1; t += 2 * blockDim.x) {
+      if (t + 1 < t1) {
+        const i64x2 x = *reinterpret_cast<const i64x2 *>(row + t);
+        h += token_term(x.x, t) + token_term(x.y, t + 1);
+      } else {
+        h += token_term(row[t], t);
+      }
+    }
+  } else {
+    for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) h += token_term(row[t], t);
+  }
+  __shared__ uint64_t wsum[4];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) h += __shfl_xor(h, off, 64);
-  if (__lane_id() == 0) part[threadIdx.x / 64] = h;
+  if (__lane_id() == 0) wsum[threadIdx.x / 64] = h;
   __syncthreads();
-  if (threadIdx.x == 0) hash[b] = part[0] + part[1] + part[2] + part[3];
+  if (threadIdx.x == 0) part[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+__device__ inline uint64_t row_hash(const uint64_t *__restrict__ part, int nch, int r) {
+  uint64_t h = 0;
+  for (int c = 0; c < nch; ++c) h += part[int64_t(r) * nch + c];
+  return h;
 }
 
 // One block per row b: rep_of[b] = the smallest c <= b whose prompt equals
 // row b's.  Candidates are scanned in ascending order in chunks of 256; only
-// equal hashes are compared in full.
-__global__ void __launch_bounds__(256) k_find_rep(const int64_t *__restrict__ ids, int64_t S, int64_t P,
-                                                   const uint64_t *__restrict__ hash,
+// equal hashes are compared in full (16-byte loads when VEC, as above).
+template <bool VEC>
+__global__ void __launch_bounds__(256) k_find_rep(const int64_t *__restrict__ ids, int64_t S, int64_t P, int nch,
+                                                   const uint64_t *__restrict__ part,
                                                    int32_t *__restrict__ rep_of) {
   const int b = blockIdx.x;
-  const uint64_t hb = hash[b];
+  const uint64_t hb = row_hash(part, nch, b);
   const int64_t *rowb = ids + int64_t(b) * S;
   __shared__ int cand[256];
   for (int c0 = 0; c0 < b; c0 += 256) {
     const int c = c0 + threadIdx.x;
-    cand[threadIdx.x] = (c < b && hash[c] == hb) ? 1 : 0;
+    cand[threadIdx.x] = (c < b && row_hash(part, nch, c) == hb) ? 1 : 0;
     __syncthreads();
     const int n = min(256, b - c0);
     for (int i = 0; i < n; ++i) {
       if (!cand[i]) continue;   // uniform: every thread reads the same flag
       const int64_t *rowc = ids + int64_t(c0 + i) * S;
       int diff = 0;
-      for (int64_t t = threadIdx.x; t < P; t += blockDim.x) diff |= (rowc[t] != rowb[t]);
+      if (VEC) {
+        const int64_t P2 = P & ~int64_t(1);
+#pragma unroll 4
+        for (int64_t t = 2 * int64_t(threadIdx.x); t < P2; t += 2 * blockDim.x) {
+          const i64x2 x = *reinterpret_cast<const i64x2 *>(rowc + t);
+          const i64x2 y = *reinterpret_cast<const i64x2 *>(rowb + t);
+          diff |= (x.x != y.x) | (x.y != y.y);
+        }
+        if ((P & 1) && threadIdx.x == 0) diff |= rowc[P - 1] != rowb[P - 1];
+      } else {
+        for (int64_t t = threadIdx.x; t < P; t += blockDim.x) diff |= (rowc[t] != rowb[t]);
+      }
       if (!__syncthreads_or(diff)) {
         if (threadIdx.x == 0) rep_of[b] = c0 + i;
         return;
@@ -185,14 +230,26 @@ __global__ void __launch_bounds__(kFinalThreads) k_finalize_groups(int B, const 
   }
 }
 
+// One block per (group slot, chunk of kHashChunk tokens): out[g] = the prompt
+// ids of group g's first member; slots g >= G exit.  VEC: S and P even, so
+// source and destination rows start on 16-byte boundaries.
+template <bool VEC>
 __global__ void __launch_bounds__(256) k_unique_prompts(const int64_t *__restrict__ ids, int64_t S, int64_t P,
-                                                         const int32_t *__restrict__ rep,
+                                                         int nch, const int32_t *__restrict__ rep,
                                                          const int32_t *__restrict__ counts,
                                                          int64_t *__restrict__ out) {
-  const int g = blockIdx.x;
+  const int g = blockIdx.x / nch;
   if (g >= counts[0]) return;
+  const int64_t t0 = int64_t(blockIdx.x % nch) * kHashChunk;
+  const int64_t t1 = t0 + kHashChunk < P ? t0 + kHashChunk : P;
   const int64_t *row = ids + int64_t(rep[g]) * S;
-  for (int64_t t = threadIdx.x; t < P; t += blockDim.x) out[int64_t(g) * P + t] = row[t];
+  int64_t *dst = out + int64_t(g) * P;
+  if (VEC) {
+    for (int64_t t = t0 + 2 * int64_t(threadIdx.x); t < t1; t += 2 * blockDim.x)
+      *reinterpret_cast<i64x2 *>(dst + t) = *reinterpret_cast<const i64x2 *>(row + t);
+  } else {
+    for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) dst[t] = row[t];
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -691,10 +748,14 @@ using namespace spd;
 // C ABI
 // ----------------------------------------------------------------------------
 
+namespace {
+// Hash chunks per row for prompts of at most P tokens (at least one).
+int64_t hash_chunks(int64_t P) { return P > kHashChunk ? (P + kHashChunk - 1) / kHashChunk : 1; }
+}  // namespace
+
 extern "C" size_t spd_group_workspace_bytes(int64_t B, int64_t S) {
-  (void)S;
-  if (B < 1) return 0;
-  return round_up(size_t(B) * 8, 256) + 3 * round_up(size_t(B) * 4, 256);
+  if (B < 1 || S < 0) return 0;
+  return round_up(size_t(B * hash_chunks(S)) * 8, 256) + 3 * round_up(size_t(B) * 4, 256);
 }
 
 extern "C" spd_status spd_group(const int64_t *input_ids, int64_t B, int64_t S, int64_t response_length,
@@ -709,24 +770,36 @@ extern "C" spd_status spd_group(const int64_t *input_ids, int64_t B, int64_t S, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t P = plan->P;
   char *ws = static_cast<char *>(workspace);
-  uint64_t *hash = reinterpret_cast<uint64_t *>(ws);
-  ws += round_up(size_t(B) * 8, 256);
+  uint64_t *hash_part = reinterpret_cast<uint64_t *>(ws);
+  ws += round_up(size_t(B * hash_chunks(S)) * 8, 256);
   int32_t *rep_of = reinterpret_cast<int32_t *>(ws);
   ws += round_up(size_t(B) * 4, 256);
   int32_t *gid_of = reinterpret_cast<int32_t *>(ws);
   ws += round_up(size_t(B) * 4, 256);
   int32_t *fill = reinterpret_cast<int32_t *>(ws);
 
-  hipLaunchKernelGGL(k_hash_rows, dim3(B), dim3(256), 0, st, input_ids, S, P, hash);
-  SPD_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_find_rep, dim3(B), dim3(256), 0, st, input_ids, S, P, hash, rep_of);
+  const int nch = static_cast<int>(hash_chunks(P));
+  const dim3 hgrid(static_cast<unsigned>(B * nch));
+  if (S % 2 == 0) {
+    hipLaunchKernelGGL(k_hash_rows<true>, hgrid, dim3(256), 0, st, input_ids, S, P, nch, hash_part);
+    SPD_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_find_rep<true>, dim3(B), dim3(256), 0, st, input_ids, S, P, nch, hash_part, rep_of);
+  } else {
+    hipLaunchKernelGGL(k_hash_rows<false>, hgrid, dim3(256), 0, st, input_ids, S, P, nch, hash_part);
+    SPD_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_find_rep<false>, dim3(B), dim3(256), 0, st, input_ids, S, P, nch, hash_part, rep_of);
+  }
   SPD_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_finalize_groups, dim3(1), dim3(kFinalThreads), 0, st, int(B), rep_of, gid_of, fill,
                      *plan);
   SPD_LAUNCH_CHECK();
   if (unique_prompts && P > 0) {
-    hipLaunchKernelGGL(k_unique_prompts, dim3(B), dim3(256), 0, st, input_ids, S, P, plan->rep, plan->counts,
-                       unique_prompts);
+    if (S % 2 == 0 && P % 2 == 0)
+      hipLaunchKernelGGL(k_unique_prompts<true>, hgrid, dim3(256), 0, st, input_ids, S, P, nch, plan->rep,
+                         plan->counts, unique_prompts);
+    else
+      hipLaunchKernelGGL(k_unique_prompts<false>, hgrid, dim3(256), 0, st, input_ids, S, P, nch, plan->rep,
+                         plan->counts, unique_prompts);
     SPD_LAUNCH_CHECK();
   }
   return SPD_OK;
