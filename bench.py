@@ -48,10 +48,11 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "0e7dae9e454b22f43683bb5200e8f0d3eeae4b56ce6262863e8b20d5bee00f9e"
+TRAFFIC_SOURCES_SHA256 = "b305afda1ca76640a60aab66db45e8cbf0a9befc6ccb0e8849b06bbbc6f01b9f"
 TRAFFIC_KIB = {   # kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
-    "fwd": (221740, 99842), "bwd_pre": (99148, 3176), "bwd_dq": (272725, 98307), "bwd_dkdv": (686706, 98685),
-    "reconstruct": (49559, 557491), "pack_rows": (49552, 98330),
+    "fwd": (221160, 99842), "bwd_pre": (99147, 3176), "bwd_dq": (272403, 98313), "bwd_dkdv": (662199, 99052),
+    "reconstruct": (49566, 557615), "pack_rows": (49552, 98318), "reconstruct_bwd": (278945, 98304),
+    "pack_rows_bwd": (51999, 557438),
 }
 
 
@@ -283,6 +284,8 @@ def main():
             kernels[kname] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
         kernels[kname]["ms_p10_p50_p90"] = kern_spread[kname]
+        if args.mode == "split":
+            kernels[kname]["traffic"] = measured_traffic(kname, name)
     # The gathers again, alone, with the 256 MB Infinity Cache flushed before each
     # call by reading a 512 MB buffer (a read leaves clean lines behind, so the
     # flush adds no write-back to the timed call; outside the timed windows).
