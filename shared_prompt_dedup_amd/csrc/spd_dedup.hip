@@ -530,6 +530,11 @@ __global__ void __launch_bounds__(kRowThreads) k_pack_rows(int64_t T, int64_t ve
 // same column t of every member of the group (read once, written n times);
 // for a response row, its own (b, t).  Then, when unpad left cells that no
 // packed row maps (counts[2] > 0), those read as zeros.
+// SOURCE_ONLY (the backward of pack_rows): only the cell row j was packed from
+// (src[j]) receives it; the other cells that map to j -- the group's other
+// members' copies of a prompt row -- receive zeros.  Written by packed row like
+// the forward, every output line is stored once.
+template <bool SOURCE_ONLY>
 __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t S, int64_t P,
                                                               int64_t vec_per_row, spd_plan plan,
                                                               const u32x4 *__restrict__ packed,
@@ -563,10 +568,11 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
       for (int m = m0; m < m1; ++m) {
         const int64_t b = every_sample ? m : (members ? members[m] : b0);
         u32x4 *o = out + (b * S + t) * vec_per_row;
+        const bool zero = SOURCE_ONLY && b != b0;
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
           const int64_t c = c0 + u * 64 + lane;
-          if (c < vec_per_row) stream_store(o + c, v[u]);
+          if (c < vec_per_row) stream_store(o + c, zero ? u32x4{0u, 0u, 0u, 0u} : v[u]);
         }
       }
     }
@@ -578,38 +584,6 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
       if (plan.dst[r] >= 0) continue;
       u32x4 *o = out + r * vec_per_row;
       for (int64_t c = lane; c < vec_per_row; c += 64) stream_store(o + c, z);
-    }
-  }
-}
-
-// Backward of pack_rows as a gather over the output: cell c = b * S + t takes
-// packed row r = dst[c] when c is that row's source (src[r] == c) and zeros
-// otherwise (another member's copy of a prompt row, or a cell no row maps).
-// Every output line is written once, in order.
-__global__ void __launch_bounds__(kRowThreads) k_pack_rows_bwd(int64_t cells, int64_t T, int64_t vec_per_row,
-                                                                const int32_t *__restrict__ dst,
-                                                                const int32_t *__restrict__ src,
-                                                                const u32x4 *__restrict__ packed,
-                                                                u32x4 *__restrict__ out) {
-  const int lane = __lane_id();
-  const int64_t nwaves = int64_t(gridDim.x) * (kRowThreads / 64);
-  for (int64_t c = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; c < cells; c += nwaves) {
-    const int64_t r = dst[c];
-    const bool ok = r >= 0 && r < T && src[r] == c;
-    const u32x4 *in = packed + (ok ? r : 0) * vec_per_row;
-    u32x4 *o = out + c * vec_per_row;
-    for (int64_t c0 = 0; c0 < vec_per_row; c0 += 64 * kU) {
-      u32x4 v[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int64_t x = c0 + u * 64 + lane;
-        v[u] = (ok && x < vec_per_row) ? in[x] : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int64_t x = c0 + u * 64 + lane;
-        if (x < vec_per_row) stream_store(o + x, v[u]);
-      }
     }
   }
 }
@@ -866,8 +840,8 @@ extern "C" spd_status spd_reconstruct(const spd_plan *plan, int64_t T, const voi
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t vpr = row_bytes / 16;
   prof_start(SPD_K_RECONSTRUCT, st);
-  hipLaunchKernelGGL(k_reconstruct, dim3(row_grid(plan->B * plan->S)), dim3(kRowThreads), 0, st, T, plan->S,
-                     plan->P, vpr, *plan, static_cast<const u32x4 *>(packed), static_cast<u32x4 *>(out));
+  hipLaunchKernelGGL(k_reconstruct<false>, dim3(row_grid(plan->B * plan->S)), dim3(kRowThreads), 0, st, T,
+                     plan->S, plan->P, vpr, *plan, static_cast<const u32x4 *>(packed), static_cast<u32x4 *>(out));
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_RECONSTRUCT, st);
   return SPD_OK;
@@ -904,9 +878,8 @@ extern "C" spd_status spd_pack_rows_bwd(const spd_plan *plan, int64_t T, const v
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t vpr = row_bytes / 16;
   prof_start(SPD_K_PACK_ROWS_BWD, st);
-  const int64_t rows = plan->B * plan->S;
-  hipLaunchKernelGGL(k_pack_rows_bwd, dim3(row_grid(rows)), dim3(kRowThreads), 0, st, rows, T, vpr, plan->dst,
-                     plan->src, static_cast<const u32x4 *>(dpacked), static_cast<u32x4 *>(drows));
+  hipLaunchKernelGGL(k_reconstruct<true>, dim3(row_grid(plan->B * plan->S)), dim3(kRowThreads), 0, st, T,
+                     plan->S, plan->P, vpr, *plan, static_cast<const u32x4 *>(dpacked), static_cast<u32x4 *>(drows));
   SPD_LAUNCH_CHECK();
   prof_stop(SPD_K_PACK_ROWS_BWD, st);
   return SPD_OK;

@@ -97,6 +97,34 @@ def test_response_length_extremes():
         _check_plan(Batch(bt.input_ids, bt.position_ids, bt.attention_mask, R, None, None), False)
 
 
+
+@pytest.mark.parametrize("S,R", [(5001, 3), (4100, 3), (6146, 2)], ids=["odd_S", "odd_P", "whole_chunks"])
+def test_grouping_across_hash_chunks(S, R):
+    """Prompts longer than one 2048-token hashing block: rows that differ in one
+    token on either side of a block boundary, in the first or last token, or by
+    two tokens swapped across a boundary never group together; exact copies do.
+    Odd S takes the 8-byte load path, odd P the odd tail of the 16-byte one."""
+    P = S - R
+    rng = np.random.default_rng(S)
+    base = rng.integers(0, 1000, size=P)
+    base[2047], base[2048] = 5, 7          # distinct, so swapping them changes the prompt
+    rows = []
+    for change in (None, P - 1, None, 2047, 2048, 0, None, 2049, 2047, P - 2, "swap"):
+        r = base.copy()
+        if change == "swap":
+            r[2047], r[2048] = r[2048], r[2047]
+        elif change is not None:
+            r[change] = r[change] + 1
+        rows.append(r)
+    B = len(rows)
+    ids = np.concatenate([np.stack(rows), rng.integers(0, 1000, size=(B, R))], axis=1).astype(np.int64)
+    pos = np.tile(np.arange(S, dtype=np.int64), (B, 1))
+    from workloads import Batch
+    bt = Batch(ids, pos, np.ones_like(ids), R, None, None)
+    say(f"[dedup plan] hash chunks S={S} P={P}")
+    oinfo, _ = _check_plan(bt, False)
+    assert oinfo["G"] == 8          # {0, 2, 6} and {3, 8} group; the other six rows stand alone
+
 ROW_CASES = [(SMALL[0], 512), (SMALL[1], 48), (SMALL[4], 16), (WORKLOADS["qwen3_0p6b_2x8_p8192_r512"], 4096),
              (WORKLOADS["long_2x8_p32768_r256to1024_unpad"], 64), (WORKLOADS["bwd_4x8_p4096_r1024"], 160)]
 
