@@ -62,20 +62,31 @@ __global__ void __launch_bounds__(256) k_bwd_pre(int Hq, int HG, int T, int Tp, 
   const int h0 = (blockIdx.x % ngrp) * HG;
   const int r0 = (blockIdx.x / ngrp) * R;
   const int sub = threadIdx.x % LPR;
-  for (int p0 = 0; p0 < R * HG; p0 += PPP) {
-    const int p = p0 + threadIdx.x / LPR;      // pair: row r0 + p / HG, head h0 + p % HG
-    const int row = r0 + p / HG, hh = p % HG;
-    float s = 0.0f;
-    if (row < T) {
-      const int64_t off = (int64_t(row) * Hq + h0 + hh) * D + sub * 8;
-      const bf16x8 a = ld_global8(o + off);
-      const bf16x8 b = ld_global8(dout + off);
+  // U passes' loads are issued before their reductions, so a thread keeps 2U
+  // loads in flight; rows past T read row 0 (T >= 1) and count as zero.
+  constexpr int U = 4;
+  for (int p0 = 0; p0 < R * HG; p0 += U * PPP) {
+    bf16x8 a[U], b[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s = fmaf(static_cast<float>(a[e]), static_cast<float>(b[e]), s);
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * PPP + threadIdx.x / LPR;   // pair: row r0 + p / HG, head h0 + p % HG
+      const int row = r0 + p / HG, hh = p % HG;
+      const int64_t off = (int64_t(row < T ? row : 0) * Hq + h0 + hh) * D + sub * 8;
+      a[u] = ld_global8(o + off);
+      b[u] = ld_global8(dout + off);
     }
 #pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (sub == 0) sD[hh * R + p / HG] = -s;
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * PPP + threadIdx.x / LPR;
+      const int row = r0 + p / HG, hh = p % HG;
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf(static_cast<float>(a[u][e]), static_cast<float>(b[u][e]), s);
+      s = row < T ? s : 0.0f;
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      if (sub == 0 && p < R * HG) sD[hh * R + p / HG] = -s;
+    }
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < HG * R; idx += blockDim.x) {
