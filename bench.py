@@ -48,11 +48,11 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "b305afda1ca76640a60aab66db45e8cbf0a9befc6ccb0e8849b06bbbc6f01b9f"
+TRAFFIC_SOURCES_SHA256 = "7063f5efaad34a0509ecd9bb747e833e505bafef2f7b1fa8473225500a723314"
 TRAFFIC_KIB = {   # kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
-    "fwd": (221160, 99842), "bwd_pre": (99147, 3176), "bwd_dq": (272403, 98313), "bwd_dkdv": (662199, 99052),
-    "reconstruct": (49566, 557615), "pack_rows": (49552, 98318), "reconstruct_bwd": (278945, 98304),
-    "pack_rows_bwd": (51999, 557438),
+    "fwd": (220360, 99914), "bwd_pre": (99173, 3176), "bwd_dq": (271537, 98318), "bwd_dkdv": (679591, 98906),
+    "reconstruct": (49566, 557550), "pack_rows": (49552, 98321), "reconstruct_bwd": (278945, 98305),
+    "pack_rows_bwd": (49570, 557483),
 }
 
 
