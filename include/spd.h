@@ -40,6 +40,10 @@
  *   gives the HIP code.
  * - Index arrays are int32 (packed rows, batch rows and (b*S+t) indices all
  *   stay below 2^31); byte offsets inside kernels are 64-bit.
+ * - A buffer with zero rows -- every [T, ...] buffer when T = 0, e.g. a batch
+ *   whose every token unpad removed -- may be NULL; the other arguments are
+ *   checked as usual, and calls that write [B, S, ...] outputs (reconstruct,
+ *   the backward of pack_rows) still write them (all zeros).
  *
  * Notation: B samples, S padded sequence length, P = S - response_length
  * prompt columns, G groups, T packed tokens, Hq / Hkv query / key-value heads,

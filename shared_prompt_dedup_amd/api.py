@@ -195,13 +195,18 @@ def pack(input_ids: torch.Tensor, position_ids: torch.Tensor, response_length: i
     return dids[:T].view(1, T), dpos[:T].view(1, T), info
 
 
+def _row_bytes(t: torch.Tensor, lead: int) -> int:
+    """Bytes of one row of ``t`` after its first ``lead`` dimensions (from the shape, so empty tensors work)."""
+    return math.prod(t.shape[lead:]) * t.element_size()
+
+
 def _pack_rows(rows: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
     plan = info.plan
     _need_cuda(rows, "rows")
     if tuple(rows.shape[:2]) != (plan.B, plan.S):
         raise ValueError("rows must be [batch, seq_len, ...]")
     tail = tuple(rows.shape[2:])
-    row_bytes = rows[0, 0].numel() * rows.element_size()
+    row_bytes = _row_bytes(rows, 2)
     out = torch.empty((plan.T,) + tail, dtype=rows.dtype, device=rows.device)
     check("spd_pack_rows", lib.spd_pack_rows(ctypes.byref(plan.c), plan.T, _ptr(rows), row_bytes, _ptr(out),
                                              _stream(rows.device)))
@@ -216,7 +221,7 @@ def pack_rows_bwd(dpacked: torch.Tensor, info: ReconstructionInfo) -> torch.Tens
     if dpacked.shape[0] != plan.T:
         raise ValueError(f"dpacked has {dpacked.shape[0]} rows, the plan has T = {plan.T}")
     tail = tuple(dpacked.shape[1:])
-    row_bytes = (dpacked[0].numel() if dpacked.dim() > 1 else 1) * dpacked.element_size()
+    row_bytes = _row_bytes(dpacked, 1)
     out = torch.empty((plan.B, plan.S) + tail, dtype=dpacked.dtype, device=dpacked.device)
     check("spd_pack_rows_bwd", lib.spd_pack_rows_bwd(ctypes.byref(plan.c), plan.T, _ptr(dpacked), row_bytes,
                                                      _ptr(out), _stream(dpacked.device)))
@@ -247,7 +252,7 @@ def _reconstruct(x: torch.Tensor, info: ReconstructionInfo) -> torch.Tensor:
     if x.shape[0] != plan.T:
         raise ValueError(f"dedup_hidden has {x.shape[0]} rows, the plan has T = {plan.T}")
     tail = tuple(x.shape[1:])
-    row_bytes = (x[0].numel() if x.dim() > 1 else 1) * x.element_size()
+    row_bytes = _row_bytes(x, 1)
     out = torch.empty((plan.B, plan.S) + tail, dtype=x.dtype, device=x.device)
     check("spd_reconstruct", lib.spd_reconstruct(ctypes.byref(plan.c), plan.T, _ptr(x), row_bytes, _ptr(out),
                                                  _stream(x.device)))
@@ -268,7 +273,7 @@ def reconstruct_bwd(dout: torch.Tensor, info: ReconstructionInfo) -> torch.Tenso
     else:
         raise TypeError("reconstruct_bwd supports bfloat16 and float32 gradients")
     tail = tuple(dout.shape[2:])
-    row_bytes = dout[0, 0].numel() * dout.element_size()
+    row_bytes = _row_bytes(dout, 2)
     out = torch.empty((plan.T,) + tail, dtype=dout.dtype, device=dout.device)
     check("spd_reconstruct_bwd", lib.spd_reconstruct_bwd(ctypes.byref(plan.c), plan.T, _ptr(dout), row_bytes, dt,
                                                          _ptr(out), _stream(dout.device)))
@@ -321,10 +326,6 @@ def create_full_batch(input_ids, position_ids, response_length, attention_mask=N
     return pack(input_ids, position_ids, response_length, groups, prompts, attention_mask, use_unpad)
 
 
-def _row_bytes(x: torch.Tensor) -> int:
-    return (x[0].numel() if x.dim() > 1 else 1) * x.element_size()
-
-
 def repack_rows(x: torch.Tensor, to_info: ReconstructionInfo, from_info: ReconstructionInfo) -> torch.Tensor:
     """spd_repack_rows: rows of ``from_info``'s packed layout ``[T_from, ...]`` -> ``to_info``'s ``[T_to, ...]``."""
     to, fr = to_info.plan, from_info.plan
@@ -333,7 +334,7 @@ def repack_rows(x: torch.Tensor, to_info: ReconstructionInfo, from_info: Reconst
         raise ValueError(f"x has {x.shape[0]} rows, the source layout has T = {fr.T}")
     out = torch.empty((to.T,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
     check("spd_repack_rows", lib.spd_repack_rows(ctypes.byref(to.c), to.T, ctypes.byref(fr.c), fr.T, _ptr(x),
-                                                 _row_bytes(x), _ptr(out), _stream(x.device)))
+                                                 _row_bytes(x, 1), _ptr(out), _stream(x.device)))
     return out
 
 
@@ -352,7 +353,7 @@ def repack_rows_bwd(dout: torch.Tensor, to_info: ReconstructionInfo, from_info: 
         raise TypeError("repack_rows_bwd supports bfloat16 and float32 gradients")
     out = torch.empty((fr.T,) + tuple(dout.shape[1:]), dtype=dout.dtype, device=dout.device)
     check("spd_repack_rows_bwd", lib.spd_repack_rows_bwd(ctypes.byref(to.c), to.T, ctypes.byref(fr.c), fr.T,
-                                                         _ptr(dout), _row_bytes(dout), dt, _ptr(out),
+                                                         _ptr(dout), _row_bytes(dout, 1), dt, _ptr(out),
                                                          _stream(dout.device)))
     return out
 

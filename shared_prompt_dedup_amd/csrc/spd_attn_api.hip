@@ -395,9 +395,9 @@ extern "C" spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_pl
                                          const void *k, const void *v, void *o, float *lse, void *workspace,
                                          size_t workspace_bytes, void *stream) {
   SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes));
+  if (T == 0) return SPD_OK;      // no rows: the [T, ...] buffers may be NULL
   if (!q || !k || !v || !o || !lse) return SPD_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return SPD_ERR_ALIGNMENT;
-  if (T == 0) return SPD_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnWs w = carve(*desc, plan->B, T, workspace);
   TileJob qj;
@@ -421,11 +421,11 @@ extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_pl
                                          const void *dout, void *dq, void *dk, void *dv, void *workspace,
                                          size_t workspace_bytes, void *stream) {
   SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes));
+  if (T == 0) return SPD_OK;      // no rows: the [T, ...] buffers may be NULL
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPD_ERR_INVALID_ARG;
   for (const void *p : {q, k, v, o, static_cast<const void *>(lse), dout, static_cast<const void *>(dq),
                         static_cast<const void *>(dk), static_cast<const void *>(dv)})
     if (!aligned16(p)) return SPD_ERR_ALIGNMENT;
-  if (T == 0) return SPD_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttnWs w = carve(*desc, plan->B, T, workspace);
   // both lists in one launch, one block each

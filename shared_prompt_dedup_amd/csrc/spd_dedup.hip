@@ -819,7 +819,7 @@ extern "C" spd_status spd_pack(const int64_t *input_ids, const int64_t *position
 extern "C" spd_status spd_pack_rows(const spd_plan *plan, int64_t T, const void *rows, int64_t row_bytes,
                                     void *packed, void *stream) {
   SPD_TRY(validate_plan(plan));
-  if (!rows || !packed || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if (!rows || (!packed && T != 0) || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
   if (row_bytes % 16 || !aligned16(rows) || !aligned16(packed)) return SPD_ERR_ALIGNMENT;
   if (T == 0) return SPD_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -835,7 +835,7 @@ extern "C" spd_status spd_pack_rows(const spd_plan *plan, int64_t T, const void 
 extern "C" spd_status spd_reconstruct(const spd_plan *plan, int64_t T, const void *packed, int64_t row_bytes,
                                       void *out, void *stream) {
   SPD_TRY(validate_plan(plan));
-  if (!packed || !out || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if ((!packed && T != 0) || !out || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
   if (row_bytes % 16 || !aligned16(packed) || !aligned16(out)) return SPD_ERR_ALIGNMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t vpr = row_bytes / 16;
@@ -850,7 +850,7 @@ extern "C" spd_status spd_reconstruct(const spd_plan *plan, int64_t T, const voi
 extern "C" spd_status spd_reconstruct_bwd(const spd_plan *plan, int64_t T, const void *dout, int64_t row_bytes,
                                           int32_t dtype, void *dpacked, void *stream) {
   SPD_TRY(validate_plan(plan));
-  if (!dout || !dpacked || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if (!dout || (!dpacked && T != 0) || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
   if (dtype != SPD_F32 && dtype != SPD_BF16) return SPD_ERR_UNSUPPORTED;
   if (row_bytes % 16 || !aligned16(dout) || !aligned16(dpacked)) return SPD_ERR_ALIGNMENT;
   if (T == 0) return SPD_OK;
@@ -873,7 +873,7 @@ extern "C" spd_status spd_reconstruct_bwd(const spd_plan *plan, int64_t T, const
 extern "C" spd_status spd_pack_rows_bwd(const spd_plan *plan, int64_t T, const void *dpacked, int64_t row_bytes,
                                         void *drows, void *stream) {
   SPD_TRY(validate_plan(plan));
-  if (!dpacked || !drows || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if ((!dpacked && T != 0) || !drows || T < 0 || T > plan->B * plan->S || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
   if (row_bytes % 16 || !aligned16(dpacked) || !aligned16(drows)) return SPD_ERR_ALIGNMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t vpr = row_bytes / 16;
@@ -926,7 +926,7 @@ spd_status validate_pair(const spd_plan *to, int64_t T_to, const spd_plan *from,
 extern "C" spd_status spd_repack_rows(const spd_plan *to, int64_t T_to, const spd_plan *from, int64_t T_from,
                                       const void *in, int64_t row_bytes, void *out, void *stream) {
   SPD_TRY(validate_pair(to, T_to, from, T_from));
-  if (!in || !out || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if ((!in && T_from != 0) || (!out && T_to != 0) || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
   if (row_bytes % 16 || !aligned16(in) || !aligned16(out)) return SPD_ERR_ALIGNMENT;
   if (T_to == 0) return SPD_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -941,7 +941,7 @@ extern "C" spd_status spd_repack_rows_bwd(const spd_plan *to, int64_t T_to, cons
                                           const void *dout, int64_t row_bytes, int32_t dtype, void *din,
                                           void *stream) {
   SPD_TRY(validate_pair(to, T_to, from, T_from));
-  if (!dout || !din || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
+  if ((!dout && T_to != 0) || (!din && T_from != 0) || row_bytes <= 0) return SPD_ERR_INVALID_ARG;
   if (dtype != SPD_F32 && dtype != SPD_BF16) return SPD_ERR_UNSUPPORTED;
   if (row_bytes % 16 || !aligned16(dout) || !aligned16(din)) return SPD_ERR_ALIGNMENT;
   if (T_from == 0) return SPD_OK;

@@ -95,6 +95,9 @@ def test_rows_calls_reject_bad_arguments():
     assert lib.spd_pack_rows(ctypes.byref(p), 33, A[12], 32, A[13], None) == INVALID  # T > B*S
     assert lib.spd_pack_rows(ctypes.byref(p), 5, A[12] + 2, 32, A[13], None) == ALIGN
     assert lib.spd_pack_rows(ctypes.byref(p), 0, A[12], 32, A[13], None) == OK       # empty: nothing to do
+    assert lib.spd_pack_rows(ctypes.byref(p), 0, A[12], 32, None, None) == OK        # zero rows may be NULL
+    assert lib.spd_pack_rows(ctypes.byref(p), 5, A[12], 32, None, None) == INVALID   # ... but only zero rows
+    assert lib.spd_reconstruct(ctypes.byref(p), 5, None, 48, A[13], None) == INVALID
     assert lib.spd_reconstruct(ctypes.byref(p), 5, A[12], 0, A[13], None) == INVALID
     assert lib.spd_reconstruct(ctypes.byref(p), 5, A[12], 48, A[13] + 8, None) == ALIGN
     assert lib.spd_reconstruct(ctypes.byref(p), -1, A[12], 48, A[13], None) == INVALID
@@ -106,6 +109,9 @@ def test_rows_calls_reject_bad_arguments():
     assert lib.spd_reconstruct_bwd(ctypes.byref(p), 5, None, 32, 1, A[13], None) == INVALID
     assert lib.spd_reconstruct_bwd(ctypes.byref(p), 5, A[12], 32, 0, A[13] + 4, None) == ALIGN
     assert lib.spd_reconstruct_bwd(ctypes.byref(p), 0, A[12], 32, 1, A[13], None) == OK       # empty
+    assert lib.spd_reconstruct_bwd(ctypes.byref(p), 0, A[12], 32, 1, None, None) == OK        # zero rows: NULL
+    assert lib.spd_reconstruct_bwd(ctypes.byref(p), 5, A[12], 32, 1, None, None) == INVALID
+    assert lib.spd_pack_rows_bwd(ctypes.byref(p), 5, None, 32, A[13], None) == INVALID
     assert lib.spd_pack_rows_bwd(ctypes.byref(p), 5, A[12], 0, A[13], None) == INVALID
     assert lib.spd_pack_rows_bwd(ctypes.byref(p), 5, A[12] + 8, 32, A[13], None) == ALIGN
     assert lib.spd_pack_rows_bwd(ctypes.byref(p), -1, A[12], 32, A[13], None) == INVALID
@@ -175,6 +181,9 @@ def test_attention_validation_order():
     assert fwd(20, [A[0], None, A[2], A[3], A[4]]) == INVALID
     assert fwd(20, [A[0], A[1] + 2, A[2], A[3], A[4]]) == ALIGN
     assert fwd(0, A[:5], lib.spd_attn_workspace_bytes(ctypes.byref(d), 4, 0)) == OK   # empty batch
+    assert fwd(0, [None] * 5, lib.spd_attn_workspace_bytes(ctypes.byref(d), 4, 0)) == OK   # zero rows may be NULL
+    assert lib.spd_split_attn_bwd(ctypes.byref(d), ctypes.byref(p), 0, *([None] * 9), A[9],
+                                  lib.spd_attn_workspace_bytes(ctypes.byref(d), 4, 0), None) == OK
     bwd = lambda ptrs: lib.spd_split_attn_bwd(ctypes.byref(d), ctypes.byref(p), 20, *ptrs, A[9], ws, None)
     assert bwd([*A[:8], None]) == INVALID
     assert bwd([*A[:8], A[8] + 8]) == ALIGN

@@ -110,6 +110,34 @@ def test_empty_prompt_and_empty_responses():
         compare(key, to_numpy(got), ref, w.dtype)
 
 
+def test_fully_masked_batch():
+    """Unpad removes every token (an all-zero mask): T = 0.  Every call takes the
+    empty packed batch; reconstruct and the backward of pack_rows write zeros."""
+    import shared_prompt_dedup_amd as spd
+    from workloads import Batch
+    w = SMALL["bf16_gqa2_ragged_unpad"]
+    b0 = make_batch(w, permute=True)
+    bt = Batch(b0.input_ids, b0.position_ids, np.zeros_like(b0.attention_mask), b0.response_length, None, None)
+    say("[attn small] every token masked: T = 0")
+    _, _, odids, _, oinfo = oracle_plan(bt, True)
+    _, _, dids, dpos, ginfo = gpu_plan(bt, True)
+    assert oinfo["T"] == 0 and ginfo["T"] == 0 and dids.numel() == 0 and dpos.numel() == 0
+    _, q, k, v, do = attn_inputs(w, 0)
+    o, lse = spd.split_attn_fwd(q, k, v, ginfo)
+    assert o.shape == q.shape and tuple(lse.shape) == (w.num_q_heads, 0)
+    dq, dk, dv = spd.split_attn_bwd(q, k, v, o, lse, do, ginfo)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+    B, S, W = w.batch, w.seq_len, w.num_q_heads * w.head_dim
+    hidden = torch.ones((B, S, W), dtype=torch.bfloat16, device="cuda")
+    packed = spd.pack_rows(hidden, ginfo)
+    assert tuple(packed.shape) == (0, W)
+    out = spd.reconstruct(o.view(0, W), ginfo)
+    assert tuple(out.shape) == (B, S, W) and not out.any()
+    assert tuple(spd.reconstruct_bwd(hidden, ginfo).shape) == (0, W)
+    back = spd.pack_rows_bwd(packed, ginfo)
+    assert tuple(back.shape) == (B, S, W) and not back.any()
+
+
 @pytest.mark.parametrize("name", ["bf16_gqa2_ragged_unpad", "bf16_split_chunks"])
 def test_backward_is_bitwise_repeatable(name):
     import shared_prompt_dedup_amd as spd

@@ -125,6 +125,19 @@ def test_grouping_across_hash_chunks(S, R):
     oinfo, _ = _check_plan(bt, False)
     assert oinfo["G"] == 8          # {0, 2, 6} and {3, 8} group; the other six rows stand alone
 
+
+def test_maximum_batch_size():
+    """B = 65,536 rows, the largest batch the C ABI takes, of 3-token prompts over a
+    3-token vocabulary: all 27 prompts occur, each group with thousands of members."""
+    rng = np.random.default_rng(65536)
+    B, P, R = 65536, 3, 1
+    ids = rng.integers(0, 3, size=(B, P + R)).astype(np.int64)
+    pos = np.tile(np.arange(P + R, dtype=np.int64), (B, 1))
+    from workloads import Batch
+    say(f"[dedup plan] maximum batch B={B}")
+    oinfo, _ = _check_plan(Batch(ids, pos, np.ones_like(ids), R, None, None), False)
+    assert oinfo["G"] == 27
+
 ROW_CASES = [(SMALL[0], 512), (SMALL[1], 48), (SMALL[4], 16), (WORKLOADS["qwen3_0p6b_2x8_p8192_r512"], 4096),
              (WORKLOADS["long_2x8_p32768_r256to1024_unpad"], 64), (WORKLOADS["bwd_4x8_p4096_r1024"], 160)]
 
