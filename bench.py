@@ -48,11 +48,11 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "7063f5efaad34a0509ecd9bb747e833e505bafef2f7b1fa8473225500a723314"
+TRAFFIC_SOURCES_SHA256 = "495996513c922f471ff2072e6ae4f93ceca370c98554305e278f5041749ada70"
 TRAFFIC_KIB = {   # kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
-    "fwd": (220360, 99914), "bwd_pre": (99173, 3176), "bwd_dq": (271537, 98318), "bwd_dkdv": (679591, 98906),
-    "reconstruct": (49566, 557550), "pack_rows": (49552, 98321), "reconstruct_bwd": (278945, 98305),
-    "pack_rows_bwd": (49570, 557483),
+    "fwd": (220365, 99890), "bwd_pre": (99173, 3176), "bwd_dq": (271508, 98347), "bwd_dkdv": (689778, 98919),
+    "reconstruct": (49566, 557547), "pack_rows": (49552, 98322), "reconstruct_bwd": (278945, 98305),
+    "pack_rows_bwd": (49568, 557490),
 }
 
 
