@@ -39,20 +39,17 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 # HBM traffic per launch from two rocprofv3 --pmc passes (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch) over `bench.py --steps 1 --warmup 1
-# --cpu-baseline off --profile-steps 1` on the default workload.  The same
-# counters read for the 1 GiB device-to-device copy in that run give the
-# scale factors (FETCH_SIZE counts half of what is read on this chip,
-# WRITE_SIZE counts exactly).  Valid only for the kernel sources hashed in
-# TRAFFIC_SOURCES: after any change there the figure is reported as null.
+# --cpu-baseline off --profile-steps 1 [--workload W]`.  The same counters
+# read for the 1 GiB device-to-device copy in that run give the scale factors
+# (FETCH_SIZE counts half of what is read on this chip, WRITE_SIZE counts
+# exactly).  Valid only for the kernel sources hashed in TRAFFIC_SOURCES:
+# after any change there the figure is reported as null.
 TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "495996513c922f471ff2072e6ae4f93ceca370c98554305e278f5041749ada70"
-TRAFFIC_KIB = {   # kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
-    "fwd": (220365, 99890), "bwd_pre": (99173, 3176), "bwd_dq": (271508, 98347), "bwd_dkdv": (689778, 98919),
-    "reconstruct": (49566, 557547), "pack_rows": (49552, 98322), "reconstruct_bwd": (278945, 98305),
-    "pack_rows_bwd": (49568, 557490),
+TRAFFIC_SOURCES_SHA256 = None     # sources the figures below were taken with (None: none taken yet)
+TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
 }
 
 
@@ -65,10 +62,11 @@ def sources_sha256():
 
 
 def measured_traffic(kernel, workload):
-    """Calibrated HBM bytes per launch, or None when not measured for these sources."""
-    if workload != BENCH_WORKLOAD or kernel not in TRAFFIC_KIB or TRAFFIC_SOURCES_SHA256 != sources_sha256():
+    """Calibrated HBM bytes per launch, or None when not measured for these sources and this workload."""
+    table = TRAFFIC_KIB.get(workload, {})
+    if kernel not in table or TRAFFIC_SOURCES_SHA256 != sources_sha256():
         return None
-    fetch, write = TRAFFIC_KIB[kernel]
+    fetch, write = table[kernel]
     return round((fetch * TRAFFIC_FETCH_SCALE + write * TRAFFIC_WRITE_SCALE) * 1024)
 
 
@@ -99,21 +97,32 @@ def attention_split(kern_ms, fwd_flops, bwd_flops):
     return out
 
 
-def cpu_baseline(w, bt, pairs_per_head, min_seconds=10.0):
-    """The oracle, as it stands, forward + backward (fp64) on query heads of the same
-    workload, one head at a time until at least `min_seconds` of CPU work."""
+def cpu_baseline(w, bt, pairs, min_seconds=10.0, max_tokens=16384):
+    """The oracle, as it stands, forward + backward (fp64), timed on a bounded slice of the same workload and
+    scaled to the whole batch.
+
+    The slice is the batch's first sample alone, cut to its first `max_tokens` tokens (a causal sequence in its
+    own right), one query head at a time until at least `min_seconds` of CPU work.  The oracle runs
+    non-deduplicated attention, so on the whole batch it does sum_b L_b (L_b + 1) / 2 (query, key) pairs per
+    head; its time there is the slice's time scaled by that count over the slice's, and `value` is the batch's
+    useful (deduplicated) FLOPs over that time, counted as on the GPU (14 d FLOP per pair and head)."""
     import oracle
-    from workloads import make_attn_inputs
+    from workloads import Batch, make_attn_inputs
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"],
                            default=1)
     except Exception:  # pragma: no cover
         blas_threads = 1
-    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
-    _, _, info = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
-                                                  attention_mask=bt.attention_mask, use_unpad=w.use_unpad)
+    S = bt.input_ids.shape[1]
+    n = min(S, max_tokens)
+    resp = max(0, bt.response_length - (S - n))       # response columns left in the first n
+    one = Batch(bt.input_ids[:1, :n], bt.position_ids[:1, :n], bt.attention_mask[:1, :n], resp, None, None)
+    groups, uniq = oracle.find_prompt_groups(one.input_ids, one.response_length)
+    _, _, info = oracle.create_deduplicated_batch(one.input_ids, one.position_ids, one.response_length, groups, uniq,
+                                                  attention_mask=one.attention_mask, use_unpad=w.use_unpad)
     x = make_attn_inputs(w, info["T"])
+    _, slice_plain = oracle.attended_pairs(info)
     heads = 0
     dt = 0.0
     while heads < w.num_q_heads and dt < min_seconds:
@@ -122,12 +131,20 @@ def cpu_baseline(w, bt, pairs_per_head, min_seconds=10.0):
         oracle.split_attention_backward(x.q, x.k, x.v, x.do, info, heads=[heads])
         dt += time.perf_counter() - t0
         heads += 1
-    flops = 14 * w.head_dim * heads * pairs_per_head
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+    # non-deduplicated pairs of the whole batch (one causal sequence per sample), counted by the oracle's plan
+    g_all, u_all = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    _, _, info_all = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, g_all,
+                                                      u_all, attention_mask=bt.attention_mask, use_unpad=w.use_unpad)
+    _, plain = oracle.attended_pairs(info_all)
+    t_full = dt * (plain * w.num_q_heads) / (slice_plain * heads)
+    useful = 14 * w.head_dim * w.num_q_heads * pairs
+    return {"value": round(useful / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle (non-deduplicated per-sample attention), forward+backward of "
-                      f"{heads} of {w.num_q_heads} query heads over the full batch; {dt:.1f} s; "
-                      f"useful FLOPs counted as on the GPU; host cores available "
+            "sample": f"fp64 numpy oracle (non-deduplicated per-sample attention), forward+backward of the batch's "
+                      f"first sample alone, its first {info['T']} tokens, {heads} of {w.num_q_heads} query heads, "
+                      f"{dt:.1f} s; scaled to the whole batch by non-deduplicated pairs ({plain} per head vs "
+                      f"{slice_plain} in the slice: {t_full:.0f} s estimated); value = the batch's deduplicated "
+                      f"useful FLOPs (14 d per pair and head) over that time; host cores available "
                       f"{len(os.sched_getaffinity(0))}, {platform.processor() or platform.machine()}"}
 
 
@@ -161,7 +178,7 @@ def main():
     import shared_prompt_dedup_amd as spd
     from workloads import WORKLOADS, make_attn_inputs, make_batch
 
-    name = args.workload or ("long_2x8_p32768_r256to1024_unpad" if args.mode == "padded_mask" else BENCH_WORKLOAD)
+    name = args.workload or BENCH_WORKLOAD
     w = WORKLOADS[name]
     use_unpad = w.use_unpad and args.mode != "padded_mask"
     assert w.dtype == "bf16"

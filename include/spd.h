@@ -102,6 +102,11 @@ typedef struct spd_plan {
                                      attention-mask entry is 0 (padded mode with a mask),
                                      counts[4] = L0, prompt columns of a shared prefix (0: none),
                                      counts[5] = packed rows of that prefix, [6..7] reserved */
+  int32_t padded_with_mask; /* host: written by spd_pack -- 1 when it packed in padded mode
+                                     (use_unpad = 0) with an attention mask, so pads may sit among
+                                     the packed rows; 0 otherwise.  The attention calls reject a
+                                     plan with this flag set (see spd_split_attn_fwd).  A caller
+                                     that has read counts[3] == 0 (no pad was kept) may clear it. */
 } spd_plan;
 
 /* ---------------------------------------------------------------- grouping */
@@ -150,11 +155,16 @@ size_t spd_pack_workspace_bytes(int64_t B, int64_t S);
  * Writes prompt_off, prompt_len, resp_off, resp_len, src, dst, seg_start,
  * counts[1] = T, counts[2] (cells left out by unpad) and counts[3] (packed
  * rows whose mask entry is 0: padded mode with a mask keeps such pads in the
- * packed sequence; attention must then treat them as absent).
+ * packed sequence, where they are no sample's tokens).  On the host it sets
+ * plan->padded_with_mask (1 for use_unpad == 0 with a mask, else 0).
+ * Attention over such a batch (Working with Packed/Unpacked Sequences: pads
+ * take no part) runs on the same batch packed with use_unpad = 1 -- a second
+ * plan with the same group arrays -- with the rows moved between the two
+ * layouts by spd_repack_rows (pads come back as zeros).
  */
 spd_status spd_pack(const int64_t *input_ids, const int64_t *position_ids,
                     const void *attention_mask, int32_t mask_elem_bytes, int32_t use_unpad,
-                    const spd_plan *plan, int64_t *dedup_ids, int64_t *dedup_pos,
+                    spd_plan *plan, int64_t *dedup_ids, int64_t *dedup_pos,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -313,14 +323,20 @@ typedef struct spd_attn_desc {
 } spd_attn_desc;
 
 /*
- * Workspace bytes the attention calls need for T packed rows of a B-sample
- * plan (the same query serves the forward and the backward).  For bf16 it
- * includes the backward's partial-sum slots for split key tiles:
- * min(64, 1024 / Hkv) slots of 256 keys x Hkv x d fp32, for dk and for dv
- * (128 MiB at Hkv 8, d 128; at most 256 MiB); the forward never touches them.
+ * Workspace bytes spd_split_attn_bwd needs for T packed rows of a B-sample
+ * plan (also enough for the forward).  For bf16 it includes the partial-sum
+ * slots for split key tiles: min(64, 1024 / Hkv) slots of 256 keys x Hkv x d
+ * fp32, for dk and for dv (128 MiB at Hkv 8, d 128; at most 256 MiB).
  * Returns 0 for an invalid descriptor, B < 1 or T < 0.
  */
 size_t spd_attn_workspace_bytes(const spd_attn_desc *desc, int64_t B, int64_t T);
+
+/*
+ * Workspace bytes spd_split_attn_fwd needs: the query-tile list and the
+ * planner's scratch only, about 100 bytes per 128 packed rows plus 8 bytes
+ * per sample.  Returns 0 for an invalid descriptor, B < 1 or T < 0.
+ */
+size_t spd_attn_fwd_workspace_bytes(const spd_attn_desc *desc, int64_t B, int64_t T);
 
 /*
  * Split attention forward ("Split Attention Optimization").  In the packed
@@ -334,8 +350,13 @@ size_t spd_attn_workspace_bytes(const spd_attn_desc *desc, int64_t B, int64_t T)
  *   lse      device float [Hq, T]  natural-log softmax denominator per row,
  *            kept for the backward
  *   T        the packed length written by spd_pack (rows >= T are never read)
+ *   workspace at least spd_attn_fwd_workspace_bytes(desc, plan->B, T) bytes
  * bf16 runs on matrix cores with fp32 accumulation and one rounding of o;
  * fp32 is a plain-arithmetic path for small problems.
+ * Limits: T * Hkv * d * (element bytes) < 2^32 (the key/value tensors stay
+ * within 4 GiB: 2,097,151 rows at Hkv 8, d 128, bf16) and Hq * T * d < 2^40,
+ * else SPD_ERR_UNSUPPORTED.  A plan with padded_with_mask set is rejected
+ * with SPD_ERR_UNSUPPORTED: its pads would otherwise be attended as tokens.
  */
 spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T,
                               const void *q, const void *k, const void *v, void *o, float *lse,
@@ -350,7 +371,8 @@ spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_plan *plan, i
  * order (a key read by very many rows is split over several blocks whose fp32
  * partial sums are added in chunk order), so results are bitwise reproducible
  * run to run.  The workspace (spd_attn_workspace_bytes) holds per-row
- * statistics, the tile lists and, for bf16, the partial-sum slots.
+ * statistics, the tile lists and, for bf16, the partial-sum slots.  Same
+ * limits and padded_with_mask rule as the forward.
  */
 spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T,
                               const void *q, const void *k, const void *v, const void *o,

@@ -248,36 +248,46 @@ def dkdv_rows(q, k, v, dout, info, keys, kv_heads, scale=None):
 
     Sums, over every sample whose sequence contains the key and every query
     position at or after it with a non-zero ``dO``, over the query heads of
-    the kv head: ``dv += P dO`` and ``dk += scale * dS q``.
+    the kv head: ``dv += P dO`` and ``dk += scale * dS q``.  The keys a
+    sample contains share one pass over its query rows from the earliest of
+    them: a row before a key has ``P = 0`` and ``dS = 0`` there (the key is in
+    its future), and a row without ``dO`` has ``dO = 0`` and ``dS = 0``, so
+    such rows add exact zeros.
     """
     q, k, v, T, Hq, Hkv, d, scale = _prep(q, k, v, scale)
     dout = np.asarray(dout, dtype=np.float64)
     ratio = Hq // Hkv
+    keys = np.asarray([int(x) for x in keys], dtype=np.int64)
     dk = np.zeros((len(keys), len(kv_heads), d))
     dv = np.zeros((len(keys), len(kv_heads), d))
     owner_all = _owner(info)
-    for a, kr in enumerate(keys):
-        kr = int(kr)
-        for b in range(info["B"]):
-            idx = sample_rows(info, b)
-            kpos = int(np.searchsorted(idx, kr))
-            if kpos >= len(idx) or idx[kpos] != kr:
-                continue                       # the key is not in this sample's sequence
-            own = owner_all[idx] == b
-            later = np.flatnonzero(own[kpos:])
-            if not len(later):
-                continue                       # no query of this sample that sees the key carries dO
-            first = kpos + int(later[0])
-            L = len(idx)
-            for c, j in enumerate(kv_heads):
-                for h in range(j * ratio, (j + 1) * ratio):
-                    Qs, Ks, Vs = q[idx, h], k[idx, j], v[idx, j]
-                    dOs = np.where(own[:, None], dout[idx, h], 0.0)
-                    for i0 in range(first, L, _BLOCK):
-                        i1 = min(L, i0 + _BLOCK)
-                        p, _, _, dS = _causal_block(Qs, Ks, Vs, i0, i1, scale, dOs)
-                        dv[a, c] += p[:, kpos] @ dOs[i0:i1]
-                        dk[a, c] += scale * (dS[:, kpos] @ Qs[i0:i1])
+    for b in range(info["B"]):
+        idx = sample_rows(info, b)
+        L = len(idx)
+        if L == 0:
+            continue
+        pos = np.searchsorted(idx, keys)
+        present = (pos < L) & (idx[np.minimum(pos, L - 1)] == keys)
+        if not present.any():
+            continue                           # no listed key is in this sample's sequence
+        sel = np.flatnonzero(present)
+        kpos = pos[sel]
+        own = owner_all[idx] == b
+        later = np.flatnonzero(own[kpos.min():])
+        if not len(later):
+            continue                           # no query of this sample that sees a key carries dO
+        first = int(kpos.min()) + int(later[0])
+        for c, j in enumerate(kv_heads):
+            for h in range(j * ratio, (j + 1) * ratio):
+                Qs, Ks, Vs = q[idx, h], k[idx, j], v[idx, j]
+                dOs = np.where(own[:, None], dout[idx, h], 0.0)
+                for i0 in range(first, L, _BLOCK):
+                    i1 = min(L, i0 + _BLOCK)
+                    p, _, _, dS = _causal_block(Qs, Ks, Vs, i0, i1, scale, dOs)
+                    seen = kpos < i1               # keys at or after i1 are in every row's future here
+                    ks, kp = sel[seen], kpos[seen]
+                    dv[ks, c] += p[:, kp].T @ dOs[i0:i1]
+                    dk[ks, c] += scale * (dS[:, kp].T @ Qs[i0:i1])
     return dk, dv
 
 

@@ -26,6 +26,7 @@ class SpdPlan(ctypes.Structure):
         ("rep", ctypes.c_void_p), ("prompt_off", ctypes.c_void_p), ("prompt_len", ctypes.c_void_p),
         ("resp_off", ctypes.c_void_p), ("resp_len", ctypes.c_void_p), ("src", ctypes.c_void_p),
         ("dst", ctypes.c_void_p), ("seg_start", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+        ("padded_with_mask", ctypes.c_int32),
     ]
 
 
@@ -63,6 +64,8 @@ _SIG = {
                                           ctypes.c_size_t, _P]),
     "spd_varlen_params": (ctypes.c_int, [ctypes.POINTER(SpdPlan), _P, _P, _P, _P, _P]),
     "spd_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SpdAttnDesc), ctypes.c_int64, ctypes.c_int64]),
+    "spd_attn_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SpdAttnDesc), ctypes.c_int64,
+                                                       ctypes.c_int64]),
     "spd_split_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SpdAttnDesc), ctypes.POINTER(SpdPlan), ctypes.c_int64,
                                           _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "spd_split_attn_bwd": (ctypes.c_int, [ctypes.POINTER(SpdAttnDesc), ctypes.POINTER(SpdPlan), ctypes.c_int64,

@@ -178,6 +178,8 @@ def pack(input_ids: torch.Tensor, position_ids: torch.Tensor, response_length: i
     plan.use_unpad = bool(use_unpad)
     plan.read_counts()
     T = plan.T
+    if plan.kept_pads == 0:
+        plan.c.padded_with_mask = 0     # a mask in padded mode, but no pad among the packed rows
     info = ReconstructionInfo(plan)
     if not use_unpad and plan.kept_pads > 0:
         twin = Plan(plan.B, plan.S, plan.P, dev)
@@ -418,8 +420,9 @@ def _desc(q: torch.Tensor, k: torch.Tensor, softmax_scale: Optional[float]) -> S
     return SpdAttnDesc(Hq, k.shape[1], d, dt, scale)
 
 
-def _attn_ws(desc: SpdAttnDesc, plan: Plan, T: int, device):
-    n = lib.spd_attn_workspace_bytes(ctypes.byref(desc), plan.B, T)
+def _attn_ws(desc: SpdAttnDesc, plan: Plan, T: int, device, forward: bool):
+    query = lib.spd_attn_fwd_workspace_bytes if forward else lib.spd_attn_workspace_bytes
+    n = query(ctypes.byref(desc), plan.B, T)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
@@ -449,7 +452,7 @@ def _attn_fwd(q, k, v, info, softmax_scale):
         raise ValueError(f"q has {T} rows, the plan has T = {plan.T}")
     o = torch.empty_like(q)
     lse = torch.empty((q.shape[1], T), dtype=torch.float32, device=q.device)
-    ws = _attn_ws(desc, plan, T, q.device)
+    ws = _attn_ws(desc, plan, T, q.device, forward=True)
     check("spd_split_attn_fwd", lib.spd_split_attn_fwd(ctypes.byref(desc), ctypes.byref(plan.c), T, _ptr(q), _ptr(k),
                                                        _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                                        _stream(q.device)))
@@ -480,7 +483,7 @@ def _attn_bwd(q, k, v, o, lse, dout, info, softmax_scale):
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    ws = _attn_ws(desc, plan, T, q.device)
+    ws = _attn_ws(desc, plan, T, q.device, forward=False)
     check("spd_split_attn_bwd", lib.spd_split_attn_bwd(ctypes.byref(desc), ctypes.byref(plan.c), T, _ptr(q), _ptr(k),
                                                        _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                                        _ptr(dv), _ptr(ws), ws.numel(), _stream(q.device)))

@@ -309,7 +309,26 @@ int q_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : fwd_
 int dq_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dq_bf16_rows_per_tile(d); }
 int k_rows(const spd_attn_desc &d) { return d.dtype == SPD_F32 ? kF32Rows : dkdv_bf16_rows_per_tile(d); }
 
-// Workspace: [-D: Hq*Tp floats][-lse/scale: Hq*Tp floats][segment ends: Tp ints]
+// Forward workspace: [query tiles][scratch tiles][counts][group offsets].
+AttnWs carve_fwd(const spd_attn_desc &d, int64_t B, int64_t T, void *base) {
+  AttnWs w;
+  w.capq = tile_capacity(B, T, q_rows(d));
+  const size_t qb = round_up(size_t(w.capq) * sizeof(Tile), 256);
+  char *p = static_cast<char *>(base);
+  size_t off = 0;
+  if (p) w.qtiles = reinterpret_cast<Tile *>(p + off);
+  off += qb;
+  if (p) w.tmp = reinterpret_cast<Tile *>(p + off);
+  off += qb;
+  if (p) w.counts = reinterpret_cast<int *>(p + off);
+  off += 256;
+  if (p) w.goff = reinterpret_cast<int *>(p + off);
+  off += round_up(size_t(B + 1) * 4, 256);
+  w.bytes = off;
+  return w;
+}
+
+// Backward workspace: [-D: Hq*Tp floats][-lse/scale: Hq*Tp floats][segment ends: Tp ints]
 //            [query tiles][key tiles][scratch tiles x 2][counts][group offsets x 2]
 //            bf16 only: [split groups][arrival counters: slots x Hkv ints]
 //                       [partial dK][partial dV] (slots x Hkv x 256 x D floats each)
@@ -372,12 +391,18 @@ spd_status validate_desc(const spd_attn_desc *d) {
   return SPD_OK;
 }
 
-spd_status validate_common(const spd_attn_desc *d, const spd_plan *plan, int64_t T, void *ws, size_t ws_bytes) {
+// Checks shared by the forward and the backward; `need` is the workspace the call requires.
+spd_status validate_common(const spd_attn_desc *d, const spd_plan *plan, int64_t T, void *ws, size_t ws_bytes,
+                           size_t need) {
   SPD_TRY(validate_desc(d));
   SPD_TRY(validate_plan(plan));
   if (T < 0 || T > plan->B * plan->S) return SPD_ERR_INVALID_ARG;
+  if (plan->padded_with_mask) return SPD_ERR_UNSUPPORTED;    // pads among the rows: attend on the unpadded plan
   if (int64_t(d->num_q_heads) * T * d->head_dim >= (int64_t(1) << 40)) return SPD_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < spd_attn_workspace_bytes(d, plan->B, T)) return SPD_ERR_WORKSPACE;
+  // K / V row offsets inside the kernels are 32-bit byte offsets from a head's first row
+  const int64_t elt = d->dtype == SPD_F32 ? 4 : 2;
+  if (T * int64_t(d->num_kv_heads) * d->head_dim * elt >= (int64_t(1) << 32)) return SPD_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < need) return SPD_ERR_WORKSPACE;
   return SPD_OK;
 }
 
@@ -391,15 +416,21 @@ extern "C" size_t spd_attn_workspace_bytes(const spd_attn_desc *desc, int64_t B,
   return carve(*desc, B, T, nullptr).bytes;
 }
 
+extern "C" size_t spd_attn_fwd_workspace_bytes(const spd_attn_desc *desc, int64_t B, int64_t T) {
+  if (validate_desc(desc) != SPD_OK || B < 1 || T < 0) return 0;
+  return carve_fwd(*desc, B, T, nullptr).bytes;
+}
+
 extern "C" spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T, const void *q,
                                          const void *k, const void *v, void *o, float *lse, void *workspace,
                                          size_t workspace_bytes, void *stream) {
-  SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes));
+  SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes,
+                          desc ? spd_attn_fwd_workspace_bytes(desc, plan ? plan->B : 0, T) : 0));
   if (T == 0) return SPD_OK;      // no rows: the [T, ...] buffers may be NULL
   if (!q || !k || !v || !o || !lse) return SPD_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return SPD_ERR_ALIGNMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  AttnWs w = carve(*desc, plan->B, T, workspace);
+  AttnWs w = carve_fwd(*desc, plan->B, T, workspace);
   TileJob qj;
   qj.rows_per_tile = q_rows(*desc);
   qj.mode = kQueryTiles;
@@ -420,7 +451,8 @@ extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_pl
                                          const void *k, const void *v, const void *o, const float *lse,
                                          const void *dout, void *dq, void *dk, void *dv, void *workspace,
                                          size_t workspace_bytes, void *stream) {
-  SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes));
+  SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes,
+                          desc ? spd_attn_workspace_bytes(desc, plan ? plan->B : 0, T) : 0));
   if (T == 0) return SPD_OK;      // no rows: the [T, ...] buffers may be NULL
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPD_ERR_INVALID_ARG;
   for (const void *p : {q, k, v, o, static_cast<const void *>(lse), dout, static_cast<const void *>(dq),

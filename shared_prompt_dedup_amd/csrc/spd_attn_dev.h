@@ -144,8 +144,8 @@ __device__ inline void dma_rows(char *tile, const __bf16 *src, int r0, int T, in
 // As dma_rows, for rows x0 .. x0 + ROWS - 1 of a virtual row space joining two
 // ranges: virtual row x < lenV is row v0 + x, later ones row u0 + x - lenV
 // (rows past T - 1 are clamped to it; the caller masks what it does not own).
-// Lane offsets are 32-bit from the head's first row: the host keeps
-// T * H * D * 2 below 4 GiB.
+// Lane offsets are 32-bit from the head's first row: the entry points
+// reject T * Hkv * D * 2 >= 4 GiB before launching.
 template <int ROWS, int D, int NW>
 __device__ inline void dma_rows2(char *tile, const __bf16 *src, int x0, int lenV, int v0, int u0, int T, int H,
                                  int hh, int wave, int lane) {

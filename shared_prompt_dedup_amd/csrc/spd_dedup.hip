@@ -786,7 +786,7 @@ extern "C" size_t spd_pack_workspace_bytes(int64_t B, int64_t S) {
 }
 
 extern "C" spd_status spd_pack(const int64_t *input_ids, const int64_t *position_ids, const void *attention_mask,
-                               int32_t mask_elem_bytes, int32_t use_unpad, const spd_plan *plan,
+                               int32_t mask_elem_bytes, int32_t use_unpad, spd_plan *plan,
                                int64_t *dedup_ids, int64_t *dedup_pos, void *workspace, size_t workspace_bytes,
                                void *stream) {
   SPD_TRY(validate_plan(plan));
@@ -802,6 +802,8 @@ extern "C" spd_status spd_pack(const int64_t *input_ids, const int64_t *position
   const int64_t B = plan->B, S = plan->S, P = plan->P;
   const int esz = attention_mask ? mask_elem_bytes : 1;
   int32_t *seg = static_cast<int32_t *>(workspace);
+  // padded format with a mask: pads may sit among the packed rows, which the attention calls must not see
+  plan->padded_with_mask = (!use_unpad && attention_mask) ? 1 : 0;
   hipLaunchKernelGGL(k_seg_lengths, dim3(B), dim3(256), 0, st, S, P, attention_mask, esz, use_unpad, *plan);
   SPD_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_seg_offsets, dim3(1), dim3(kFinalThreads), 0, st, int(B), seg, *plan);

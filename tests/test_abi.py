@@ -174,19 +174,46 @@ def test_attention_validation_order():
     p = _plan()
     d = _desc()
     ws = lib.spd_attn_workspace_bytes(ctypes.byref(d), 4, 20)
-    assert ws > 0
-    fwd = lambda T, ptrs, wsb=ws: lib.spd_split_attn_fwd(ctypes.byref(d), ctypes.byref(p), T, *ptrs, A[5], wsb, None)
-    assert fwd(20, A[:5], ws - 1) == WS
+    fws = lib.spd_attn_fwd_workspace_bytes(ctypes.byref(d), 4, 20)
+    assert 0 < fws < ws
+    fwd = lambda T, ptrs, wsb=fws: lib.spd_split_attn_fwd(ctypes.byref(d), ctypes.byref(p), T, *ptrs, A[5], wsb,
+                                                          None)
+    assert fwd(20, A[:5], fws - 1) == WS
     assert fwd(33, A[:5]) == INVALID     # T > B*S
     assert fwd(20, [A[0], None, A[2], A[3], A[4]]) == INVALID
     assert fwd(20, [A[0], A[1] + 2, A[2], A[3], A[4]]) == ALIGN
-    assert fwd(0, A[:5], lib.spd_attn_workspace_bytes(ctypes.byref(d), 4, 0)) == OK   # empty batch
-    assert fwd(0, [None] * 5, lib.spd_attn_workspace_bytes(ctypes.byref(d), 4, 0)) == OK   # zero rows may be NULL
+    assert fwd(0, A[:5], lib.spd_attn_fwd_workspace_bytes(ctypes.byref(d), 4, 0)) == OK   # empty batch
+    assert fwd(0, [None] * 5, lib.spd_attn_fwd_workspace_bytes(ctypes.byref(d), 4, 0)) == OK   # zero rows: NULL
+    assert lib.spd_split_attn_bwd(ctypes.byref(d), ctypes.byref(p), 20, *A[:9], A[9], ws - 1, None) == WS
     assert lib.spd_split_attn_bwd(ctypes.byref(d), ctypes.byref(p), 0, *([None] * 9), A[9],
                                   lib.spd_attn_workspace_bytes(ctypes.byref(d), 4, 0), None) == OK
     bwd = lambda ptrs: lib.spd_split_attn_bwd(ctypes.byref(d), ctypes.byref(p), 20, *ptrs, A[9], ws, None)
     assert bwd([*A[:8], None]) == INVALID
     assert bwd([*A[:8], A[8] + 8]) == ALIGN
+
+
+def test_attention_rejects_kv_beyond_4gib():
+    """K / V row offsets in the kernels are 32-bit: T * Hkv * d * element bytes must stay below 2^32.  The limit
+    is checked before the workspace, so a missing workspace tells which side of it a size falls on."""
+    p = _plan(B=64, S=65536, P=65000)
+    for dt, elt in ((1, 2), (0, 4)):
+        d = _desc(dtype=dt)
+        limit = (1 << 32) // (8 * 128 * elt)           # first T that reaches 4 GiB of K (Hkv 8, d 128)
+        for T, code in ((limit, UNSUPPORTED), (limit - 1, WS)):
+            assert lib.spd_split_attn_fwd(ctypes.byref(d), ctypes.byref(p), T, *A[:5], None, 0, None) == code
+            assert lib.spd_split_attn_bwd(ctypes.byref(d), ctypes.byref(p), T, *A[:9], None, 0, None) == code
+
+
+def test_attention_rejects_padded_plan_with_mask():
+    """A plan packed in the padded format with an attention mask may hold pads among its rows; the attention
+    calls refuse it (the caller runs attention on the unpadded plan of the same groups)."""
+    d = _desc()
+    p = _plan(padded_with_mask=1)
+    fws = lib.spd_attn_fwd_workspace_bytes(ctypes.byref(d), 4, 20)
+    ws = lib.spd_attn_workspace_bytes(ctypes.byref(d), 4, 20)
+    assert lib.spd_split_attn_fwd(ctypes.byref(d), ctypes.byref(p), 20, *A[:5], A[5], fws, None) == UNSUPPORTED
+    assert lib.spd_split_attn_bwd(ctypes.byref(d), ctypes.byref(p), 20, *A[:9], A[9], ws, None) == UNSUPPORTED
+    assert lib.spd_split_attn_fwd(ctypes.byref(d), ctypes.byref(p), 0, *([None] * 5), A[5], fws, None) == UNSUPPORTED
 
 
 def test_workspace_grows_with_sizes():

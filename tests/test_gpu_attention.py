@@ -214,7 +214,7 @@ def test_full_forward_sampled(full):
     c, name = full, full["name"]
     w, info, x = c["w"], c["oinfo"], c["x"]
     rows = _sample_rows(info, np.random.default_rng(1), n_random=48)
-    heads = [0, w.num_q_heads - 1]
+    heads = list(range(w.num_q_heads))
     say(f"[attn full] {name}: forward on {len(rows)} rows x {len(heads)} heads")
     ro, rl = oracle.forward_rows(x["q"], x["k"], x["v"], info, rows, heads)
     go = to_numpy(c["o"])[rows][:, heads]
@@ -223,32 +223,68 @@ def test_full_forward_sampled(full):
     compare("lse", gl, rl, "bf16")
 
 
-def test_full_backward_sampled(full):
+def test_full_dq_sampled(full):
     c, name = full, full["name"]
     w, info, x = c["w"], c["oinfo"], c["x"]
-    rng = np.random.default_rng(2)
-    rows = _sample_rows(info, rng, n_random=40)
-    heads = [1, w.num_q_heads - 2]
-    say(f"[attn full] {name}: dq on {len(rows)} rows")
+    rows = _sample_rows(info, np.random.default_rng(2), n_random=40)
+    heads = list(range(w.num_q_heads))
+    say(f"[attn full] {name}: dq on {len(rows)} rows x {len(heads)} heads")
     rdq = oracle.dq_rows(x["q"], x["k"], x["v"], x["do"], info, rows, heads)
     compare("dq", to_numpy(c["dq"])[rows][:, heads], rdq, "bf16")
-    # keys: the last rows of each prompt (read by every response of the group) and response keys
+
+
+def _dkdv_check(c, keys, kvh, label):
+    w, info, x = c["w"], c["oinfo"], c["x"]
+    keys = sorted(set(int(k) for k in keys))
+    say(f"[attn full] {c['name']}: dk/dv on {len(keys)} {label} keys x kv heads {kvh}")
+    rdk, rdv = oracle.dkdv_rows(x["q"], x["k"], x["v"], x["do"], info, keys, kvh)
+    compare(f"dk ({label})", to_numpy(c["dk"])[keys][:, kvh], rdk, "bf16")
+    compare(f"dv ({label})", to_numpy(c["dv"])[keys][:, kvh], rdv, "bf16")
+
+
+def test_full_dkdv_response_keys(full):
+    """Response keys (read by the later rows of their own response only), every kv head."""
+    c = full
+    info = c["oinfo"]
+    keys = []
+    for b in range(info["B"]):
+        ro, rl = int(info["resp_off"][b]), int(info["resp_len"][b])
+        if rl:
+            keys += [ro, ro + rl // 2, ro + rl - 1]
+    _dkdv_check(c, keys, list(range(c["w"].num_kv_heads)), "response")
+
+
+def test_full_dkdv_prompt_end_keys(full):
+    """The last keys of each prompt: read by the prompt's last rows and every response row of the group."""
+    c = full
+    info, w = c["oinfo"], c["w"]
     keys = []
     for g in range(info["G"]):
         po, pl = int(info["prompt_off"][g]), int(info["prompt_len"][g])
         keys += [po + pl - 1, po + pl - 2]
-    for b in range(min(info["B"], 2)):
-        ro, rl = int(info["resp_off"][b]), int(info["resp_len"][b])
-        if rl:
-            keys += [ro, ro + rl // 2, ro + rl - 1]
-    if w.prompt_len <= 4096:
-        keys.append(int(info["prompt_off"][0]))          # the key every row of group 0 reads
-    keys = sorted(set(keys))
-    kvh = [0, w.num_kv_heads - 1]
-    say(f"[attn full] {name}: dk/dv on {len(keys)} keys")
-    rdk, rdv = oracle.dkdv_rows(x["q"], x["k"], x["v"], x["do"], info, keys, kvh)
-    compare("dk", to_numpy(c["dk"])[keys][:, kvh], rdk, "bf16")
-    compare("dv", to_numpy(c["dv"])[keys][:, kvh], rdv, "bf16")
+    # each response row's softmax spans the whole prompt: at 32K-token prompts two kv heads, else all
+    kvh = [0, w.num_kv_heads - 1] if w.prompt_len > 16384 else list(range(w.num_kv_heads))
+    _dkdv_check(c, keys, kvh, "prompt-end")
+
+
+def test_full_dkdv_first_key_of_every_prompt_tile(full):
+    """The first key of every 256-key prompt tile of the backward: the keys with the most readers (the rest of
+    their prompt and every response of the group), among them every tile the planner cuts into chunks whose fp32
+    partial sums are added afterwards.  One oracle pass per sample covers all of them; its cost grows with the
+    square of the prompt, so the kv heads checked shrink as prompts grow."""
+    c = full
+    info, w = c["oinfo"], c["w"]
+    keys = []
+    for g in range(info["G"]):
+        po, pl = int(info["prompt_off"][g]), int(info["prompt_len"][g])
+        keys += list(range(po, po + pl, 256))
+    if w.prompt_len > 16384:
+        kvh = [w.num_kv_heads // 2]
+    elif w.prompt_len > 4096:
+        kvh = [0, w.num_kv_heads - 1]
+    else:
+        kvh = list(range(w.num_kv_heads))
+    _dkdv_check(c, keys, kvh, "tile-first")
 
 
 def test_full_gradient_invariants(full):

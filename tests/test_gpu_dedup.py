@@ -193,6 +193,90 @@ def test_repeat_calls_are_identical():
         assert torch.equal(getattr(a[4].plan, f), getattr(b[4].plan, f))
 
 
+# ---------------------------------------------------------------- every row move at the workloads' own width
+
+FULL_WIDTH = ["redundancy_1x10_p10240_r1024", "long_2x8_p32768_r256to1024_unpad", "bwd_4x8_p4096_r1024",
+              "prefix_4x8_s4096_p5120_r512"]
+
+
+def _bf16_bits(rng, shape):
+    """Seeded normal values rounded to bf16: (uint16 bit patterns, float32 values); drawn one leading row at a
+    time to bound host memory."""
+    from workloads import round_to_bf16
+    bits = np.empty(shape, dtype=np.uint16)
+    for i in range(shape[0]):
+        bits[i] = round_to_bf16(rng.standard_normal(shape[1:], dtype=np.float32))[0]
+    return bits
+
+
+def _as_f32(bits):
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@pytest.mark.parametrize("name", FULL_WIDTH)
+def test_row_moves_at_full_width(name):
+    """pack_rows, reconstruct and both backwards on the attention output's own rows (Hq * d bf16 = 4096 bytes):
+    the whole batch on the GPU in one call each, compared with the oracle on column blocks (each block of a row
+    move is the same move at a narrower width), so host memory stays bounded.  The 32K-prompt batch's
+    reconstruct writes 2.2 GB: byte offsets past 2^31.  Byte moves bit-exact; reconstruct_bwd within the
+    fp32-accumulation bound of test_rows_backward."""
+    import shared_prompt_dedup_amd as spd
+    w = WORKLOADS[name]
+    say(f"[rows full width] {name}")
+    bt = make_batch(w, permute=True)
+    groups, uniq = oracle.find_prompt_groups(bt.input_ids, bt.response_length)
+    L0 = oracle.find_shared_prefix(bt.input_ids, bt.response_length, groups) if w.shared_prefix else 0
+    _, _, oinfo = oracle.create_deduplicated_batch(bt.input_ids, bt.position_ids, bt.response_length, groups, uniq,
+                                                   attention_mask=bt.attention_mask, use_unpad=w.use_unpad,
+                                                   prefix_len=L0)
+    ids, pos, mask = (torch.from_numpy(a).cuda() for a in (bt.input_ids, bt.position_ids, bt.attention_mask))
+    gg, gu = spd.find_prompt_groups(ids, bt.response_length)
+    _, _, ginfo = spd.create_deduplicated_batch(ids, pos, bt.response_length, gg, gu,
+                                                attention_mask=mask if w.use_unpad else None,
+                                                use_unpad=w.use_unpad, share_prefix=bool(w.shared_prefix))
+    assert ginfo["prefix_len"] == oinfo["prefix_len"] and (oinfo["prefix_len"] > 0) == bool(w.shared_prefix)
+    B, S, T = oinfo["B"], oinfo["S"], oinfo["T"]
+    assert ginfo["T"] == T
+    W = w.num_q_heads * w.head_dim          # bf16 elements per row: 4096 bytes
+    nmax = B if oinfo["prefix_len"] else max(len(m) for m in groups)   # terms summed into one packed row
+    blocks = [(c, c + 256) for c in range(0, W, 256)]
+    rng = np.random.default_rng(17)
+
+    # forward pair: reconstruct [T, W] -> [B, S, W]; pack_rows [B, S, W] -> [T, W]
+    packed = _bf16_bits(rng, (T, W))
+    out = spd.reconstruct_sequences(torch.from_numpy(packed.view(np.int16)).cuda().view(torch.bfloat16)[None], ginfo)
+    say(f"  reconstruct: {out.numel() * 2 / 1e9:.2f} GB written")
+    for c0, c1 in blocks:
+        ref = oracle.reconstruct_sequences(packed[:, c0:c1][None], oinfo)
+        got = out[:, :, c0:c1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, ref)
+    del out
+    rows = _bf16_bits(rng, (B, S, W))
+    rows_t = torch.from_numpy(rows.view(np.int16)).cuda().view(torch.bfloat16)
+    got = spd.pack_rows(rows_t, ginfo).view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, oracle.pack_rows(rows, oinfo))
+    del got
+    # backward pair: pack_rows_bwd [T, W] -> [B, S, W]; reconstruct_bwd [B, S, W] -> [T, W]
+    back = spd.pack_rows_bwd(torch.from_numpy(packed.view(np.int16)).cuda().view(torch.bfloat16), ginfo)
+    for c0, c1 in blocks:
+        ref = oracle.pack_rows_backward(packed[:, c0:c1], oinfo)
+        got = back[:, :, c0:c1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, ref)
+    del back
+    gsum = spd.reconstruct_bwd(rows_t, ginfo).float().cpu().numpy()
+    del rows_t
+    worst = 0.0
+    for c0, c1 in blocks:
+        vals = _as_f32(rows[:, :, c0:c1])
+        ref = oracle.reconstruct_backward(vals, oinfo)
+        absum = oracle.reconstruct_backward(np.abs(vals), oinfo)
+        bound = (nmax - 1) * 2.0**-24 * absum + 2.0**-8 * np.abs(ref)
+        err = np.abs(gsum[:, c0:c1] - ref)
+        worst = max(worst, float((err / (bound + 1e-30)).max()) if err.size else 0.0)
+        assert (err <= bound + 1e-30).all()
+    say(f"  reconstruct_bwd: worst err / bound = {worst:.3f}")
+
+
 # ---------------------------------------------------------------- backward of reconstruct / pack_rows
 
 BWD_ROW_CASES = [(SMALL[0], 512), (SMALL[1], 48), (SMALL[2], 32), (SMALL[4], 16),

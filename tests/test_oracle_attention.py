@@ -194,6 +194,35 @@ def test_sampled_rows_match_full():
     dk_s, dv_s = oracle.dkdv_rows(x.q, x.k, x.v, x.do, info, rows, [0, 1])
     np.testing.assert_allclose(dk_s, dk[rows], atol=1e-12)
     np.testing.assert_allclose(dv_s, dv[rows], atol=1e-12)
+    # every key at once, in a scrambled order: the keys of a sample share one pass over its rows
+    every = np.random.default_rng(2).permutation(info["T"])
+    dk_a, dv_a = oracle.dkdv_rows(x.q, x.k, x.v, x.do, info, every, [1, 0])
+    np.testing.assert_allclose(dk_a, dk[every][:, [1, 0]], atol=1e-12)
+    np.testing.assert_allclose(dv_a, dv[every][:, [1, 0]], atol=1e-12)
+
+
+def test_sampled_keys_match_full_across_row_blocks():
+    """Sequences of several 512-row blocks: a key read by later blocks only, keys in every block."""
+    w = WORKLOADS["tiny_fp32"].scaled(name="blocks", num_prompts=2, rollout_n=2, prompt_len=700, response_len=400,
+                                      num_q_heads=2, num_kv_heads=1, head_dim=8, resp_len_range=(100, 400), seed=77)
+    info, x = _setup(w, permute=True)
+    _, dk, dv = oracle.split_attention_backward(x.q, x.k, x.v, x.do, info)
+    keys = np.random.default_rng(6).permutation(info["T"])[:300]
+    keys = np.concatenate([keys, [int(info["prompt_off"][0]), int(info["prompt_off"][1]) + 650]])
+    dk_s, dv_s = oracle.dkdv_rows(x.q, x.k, x.v, x.do, info, keys, [0])
+    np.testing.assert_allclose(dk_s, dk[keys], atol=1e-11)
+    np.testing.assert_allclose(dv_s, dv[keys], atol=1e-11)
+
+
+def test_sampled_keys_match_full_with_shared_prefix():
+    """Prefix keys are read by every sample; the batched key pass must collect all of them."""
+    _, _, info = _prefix_setup()
+    q, k, v, do = _qkv(info["T"])
+    _, dk, dv = oracle.split_attention_backward(q, k, v, do, info)
+    keys = np.random.default_rng(4).permutation(info["T"])
+    dk_s, dv_s = oracle.dkdv_rows(q, k, v, do, info, keys, [0, 1])
+    np.testing.assert_allclose(dk_s, dk[keys], atol=1e-12)
+    np.testing.assert_allclose(dv_s, dv[keys], atol=1e-12)
 
 
 def test_attended_pairs_brute_force():

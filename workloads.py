@@ -91,8 +91,9 @@ WORKLOADS = {
         shared_prefix=4096),
 }
 
-# The single-GPU workload that throughput is quoted on.
-BENCH_WORKLOAD = "qwen3_0p6b_2x8_p8192_r512"
+# The single-GPU workload that throughput is quoted on: the largest one (32K-token prompts, about 1.4e9 attended
+# pairs).  The other bf16 workloads are measured with bench.py --workload.
+BENCH_WORKLOAD = "long_2x8_p32768_r256to1024_unpad"
 
 
 @dataclass
