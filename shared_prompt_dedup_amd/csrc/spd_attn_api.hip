@@ -391,9 +391,8 @@ spd_status validate_desc(const spd_attn_desc *d) {
   return SPD_OK;
 }
 
-// Checks shared by the forward and the backward; `need` is the workspace the call requires.
-spd_status validate_common(const spd_attn_desc *d, const spd_plan *plan, int64_t T, void *ws, size_t ws_bytes,
-                           size_t need) {
+// Checks shared by the forward and the backward (everything but the workspace).
+spd_status validate_common(const spd_attn_desc *d, const spd_plan *plan, int64_t T) {
   SPD_TRY(validate_desc(d));
   SPD_TRY(validate_plan(plan));
   if (T < 0 || T > plan->B * plan->S) return SPD_ERR_INVALID_ARG;
@@ -402,8 +401,28 @@ spd_status validate_common(const spd_attn_desc *d, const spd_plan *plan, int64_t
   // K / V row offsets inside the kernels are 32-bit byte offsets from a head's first row
   const int64_t elt = d->dtype == SPD_F32 ? 4 : 2;
   if (T * int64_t(d->num_kv_heads) * d->head_dim * elt >= (int64_t(1) << 32)) return SPD_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < need) return SPD_ERR_WORKSPACE;
   return SPD_OK;
+}
+
+// The forward after validation: the query-tile list in `workspace`, then the attention kernel.
+spd_status fwd_launch(const spd_attn_desc *desc, const spd_plan *plan, int64_t T, const void *q, const void *k,
+                      const void *v, void *o, float *lse, void *workspace, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AttnWs w = carve_fwd(*desc, plan->B, T, workspace);
+  TileJob qj;
+  qj.rows_per_tile = q_rows(*desc);
+  qj.mode = kQueryTiles;
+  qj.cap = int(w.capq);
+  qj.goff = w.goff;
+  qj.tmp = w.tmp;
+  qj.out = w.qtiles;
+  qj.n_out = w.counts;
+  SPD_TRY(launch_build_tiles(*plan, T, qj, st));
+  if (desc->dtype == SPD_F32)
+    return attn_fwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, static_cast<const float *>(q),
+                        static_cast<const float *>(k), static_cast<const float *>(v), static_cast<float *>(o), lse,
+                        st);
+  return attn_fwd_bf16(*desc, *plan, T, w.qtiles, w.counts, w.capq, q, k, v, o, lse, st);
 }
 
 }  // namespace
@@ -424,35 +443,20 @@ extern "C" size_t spd_attn_fwd_workspace_bytes(const spd_attn_desc *desc, int64_
 extern "C" spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T, const void *q,
                                          const void *k, const void *v, void *o, float *lse, void *workspace,
                                          size_t workspace_bytes, void *stream) {
-  SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes,
-                          desc ? spd_attn_fwd_workspace_bytes(desc, plan ? plan->B : 0, T) : 0));
+  SPD_TRY(validate_common(desc, plan, T));
+  if (!workspace || workspace_bytes < spd_attn_fwd_workspace_bytes(desc, plan->B, T)) return SPD_ERR_WORKSPACE;
   if (T == 0) return SPD_OK;      // no rows: the [T, ...] buffers may be NULL
   if (!q || !k || !v || !o || !lse) return SPD_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return SPD_ERR_ALIGNMENT;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  AttnWs w = carve_fwd(*desc, plan->B, T, workspace);
-  TileJob qj;
-  qj.rows_per_tile = q_rows(*desc);
-  qj.mode = kQueryTiles;
-  qj.cap = int(w.capq);
-  qj.goff = w.goff;
-  qj.tmp = w.tmp;
-  qj.out = w.qtiles;
-  qj.n_out = w.counts;
-  SPD_TRY(launch_build_tiles(*plan, T, qj, st));
-  if (desc->dtype == SPD_F32)
-    return attn_fwd_f32(*desc, *plan, T, w.qtiles, w.counts, w.capq, static_cast<const float *>(q),
-                        static_cast<const float *>(k), static_cast<const float *>(v), static_cast<float *>(o), lse,
-                        st);
-  return attn_fwd_bf16(*desc, *plan, T, w.qtiles, w.counts, w.capq, q, k, v, o, lse, st);
+  return fwd_launch(desc, plan, T, q, k, v, o, lse, workspace, stream);
 }
 
 extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T, const void *q,
                                          const void *k, const void *v, const void *o, const float *lse,
                                          const void *dout, void *dq, void *dk, void *dv, void *workspace,
                                          size_t workspace_bytes, void *stream) {
-  SPD_TRY(validate_common(desc, plan, T, workspace, workspace_bytes,
-                          desc ? spd_attn_workspace_bytes(desc, plan ? plan->B : 0, T) : 0));
+  SPD_TRY(validate_common(desc, plan, T));
+  if (!workspace || workspace_bytes < spd_attn_workspace_bytes(desc, plan->B, T)) return SPD_ERR_WORKSPACE;
   if (T == 0) return SPD_OK;      // no rows: the [T, ...] buffers may be NULL
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPD_ERR_INVALID_ARG;
   for (const void *p : {q, k, v, o, static_cast<const void *>(lse), dout, static_cast<const void *>(dq),
