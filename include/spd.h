@@ -363,6 +363,27 @@ spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_plan *plan, i
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * spd_split_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It allocates nothing (no hipMalloc, no
+ * allocating library routine); its scratch -- the query-tile list -- lives in
+ * a fixed device array of 4 MiB (4,194,304 bytes) inside the library, one
+ * per device, held until the process ends.  The
+ * caller still passes every input and output.  Same arguments, rules and
+ * results (bitwise) as spd_split_attn_fwd; sizes whose forward workspace
+ * (spd_attn_fwd_workspace_bytes) exceeds the array return SPD_ERR_WORKSPACE
+ * (e.g. about 2.7 million packed rows at 8 query heads per kv head, fewer
+ * with many samples: 8 bytes per sample).  The first call on a device looks
+ * up the array's address there (SPD_ERR_HIP if that fails).  Every call on one
+ * device shares the array: calls that overlap on one device (different
+ * streams, or threads without ordering) race and must be serialised by the
+ * caller; calls in order on one stream are safe.
+ */
+spd_status spd_split_attn_fwd_noalloc(const spd_attn_desc *desc, const spd_plan *plan, int64_t T,
+                                      const void *q, const void *k, const void *v, void *o, float *lse,
+                                      void *stream);
+
+/*
  * Split attention backward ("Correctness & Gradients").  Given o and lse from
  * the forward and dout = dL/do, writes dq [T, Hq, d], dk, dv [T, Hkv, d].
  * A prompt key's dk / dv sum over the prompt's own causal queries and every

@@ -68,6 +68,8 @@ _SIG = {
                                                        ctypes.c_int64]),
     "spd_split_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SpdAttnDesc), ctypes.POINTER(SpdPlan), ctypes.c_int64,
                                           _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "spd_split_attn_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(SpdAttnDesc), ctypes.POINTER(SpdPlan),
+                                                  ctypes.c_int64, _P, _P, _P, _P, _P, _P]),
     "spd_split_attn_bwd": (ctypes.c_int, [ctypes.POINTER(SpdAttnDesc), ctypes.POINTER(SpdPlan), ctypes.c_int64,
                                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "spd_profile_begin": (ctypes.c_int, []),

@@ -459,6 +459,28 @@ def _attn_fwd(q, k, v, info, softmax_scale):
     return o, lse
 
 
+def split_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, info: ReconstructionInfo,
+                           softmax_scale: Optional[float] = None):
+    """spd_split_attn_fwd_noalloc: as ``split_attn_fwd`` (same results), with the library's fixed device scratch
+    instead of a workspace, so only ``o`` and ``lse`` are allocated here.  Not for padded-format plans that kept
+    pads (the C call refuses them)."""
+    plan = info.plan
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda(t, name)
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v must share a dtype")
+    desc = _desc(q, k, softmax_scale)
+    T = q.shape[0]
+    if T != plan.T:
+        raise ValueError(f"q has {T} rows, the plan has T = {plan.T}")
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], T), dtype=torch.float32, device=q.device)
+    check("spd_split_attn_fwd_noalloc", lib.spd_split_attn_fwd_noalloc(ctypes.byref(desc), ctypes.byref(plan.c), T,
+                                                                       _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                                       _stream(q.device)))
+    return o, lse
+
+
 def split_attn_bwd(q, k, v, o, lse, dout, info: ReconstructionInfo, softmax_scale: Optional[float] = None):
     """spd_split_attn_bwd: ``(dq, dk, dv)`` from the forward's ``o``, ``lse`` and ``dout`` (for a padded-format
     plan that kept pads, computed in the unpadded layout; the pads' gradients are 0)."""

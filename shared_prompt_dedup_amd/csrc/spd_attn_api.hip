@@ -5,8 +5,18 @@
 // and itself) and "Correctness & Gradients".
 #include <algorithm>
 #include <climits>
+#include <mutex>
+#include <vector>
 
 #include "spd_attn.h"
+
+// Scratch of spd_split_attn_fwd_noalloc: the forward's query-tile list and the
+// planner's scratch, in place of a caller workspace.  Each device the library
+// runs on holds its own copy until the process ends.  Host code never passes
+// this name to a kernel: it is a host-side stand-in, and the device address
+// comes from hipGetSymbolAddress (noalloc_scratch below).
+static constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 namespace spd {
 
@@ -425,6 +435,32 @@ spd_status fwd_launch(const spd_attn_desc *desc, const spd_plan *plan, int64_t T
   return attn_fwd_bf16(*desc, *plan, T, w.qtiles, w.counts, w.capq, q, k, v, o, lse, st);
 }
 
+// The scratch array's address on the current device, looked up once per
+// device (with that device current) and kept.
+spd_status noalloc_scratch(void **out) {
+  static std::mutex mu;
+  static std::vector<void *> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_last_hip_error(e);
+    return SPD_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= static_cast<int>(addr.size())) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_last_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return SPD_ERR_HIP;
+    }
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return SPD_OK;
+}
+
 }  // namespace
 }  // namespace spd
 
@@ -449,6 +485,20 @@ extern "C" spd_status spd_split_attn_fwd(const spd_attn_desc *desc, const spd_pl
   if (!q || !k || !v || !o || !lse) return SPD_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return SPD_ERR_ALIGNMENT;
   return fwd_launch(desc, plan, T, q, k, v, o, lse, workspace, stream);
+}
+
+extern "C" spd_status spd_split_attn_fwd_noalloc(const spd_attn_desc *desc, const spd_plan *plan, int64_t T,
+                                                 const void *q, const void *k, const void *v, void *o, float *lse,
+                                                 void *stream) {
+  SPD_TRY(validate_common(desc, plan, T));
+  if (spd_attn_fwd_workspace_bytes(desc, plan->B, T) > kNoAllocScratchBytes) return SPD_ERR_WORKSPACE;
+  if (T == 0) return SPD_OK;      // no rows: the [T, ...] buffers may be NULL
+  if (!q || !k || !v || !o || !lse) return SPD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return SPD_ERR_ALIGNMENT;
+  void *ws = nullptr;
+  SPD_TRY(noalloc_scratch(&ws));
+  // every scratch word the planner reads it writes first in the same call: nothing to clear
+  return fwd_launch(desc, plan, T, q, k, v, o, lse, ws, stream);
 }
 
 extern "C" spd_status spd_split_attn_bwd(const spd_attn_desc *desc, const spd_plan *plan, int64_t T, const void *q,

@@ -216,6 +216,24 @@ def test_attention_rejects_padded_plan_with_mask():
     assert lib.spd_split_attn_fwd(ctypes.byref(d), ctypes.byref(p), 0, *([None] * 5), A[5], fws, None) == UNSUPPORTED
 
 
+def test_noalloc_forward_rejects_before_touching_the_device():
+    """The workspace-free forward validates like the forward and refuses sizes whose workspace exceeds its fixed
+    4 MiB scratch -- all before any HIP call."""
+    d = _desc()
+    call = lambda plan, T, ptrs: lib.spd_split_attn_fwd_noalloc(ctypes.byref(d), ctypes.byref(plan), T, *ptrs, None)
+    p = _plan()
+    assert call(p, 33, A[:5]) == INVALID                          # T > B*S
+    assert call(p, 20, [A[0], None, A[2], A[3], A[4]]) == INVALID
+    assert call(p, 20, [A[0], A[1] + 2, A[2], A[3], A[4]]) == ALIGN
+    assert call(_plan(padded_with_mask=1), 20, A[:5]) == UNSUPPORTED
+    assert call(p, 0, [None] * 5) == OK                           # empty batch: nothing to do
+    mqa = _desc(num_q_heads=1, num_kv_heads=1)
+    big = _plan(B=65536, S=32, P=16)                               # 8 bytes of planner scratch per sample
+    need = lib.spd_attn_fwd_workspace_bytes(ctypes.byref(mqa), 65536, 1000)
+    assert need > 4 << 20
+    assert lib.spd_split_attn_fwd_noalloc(ctypes.byref(mqa), ctypes.byref(big), 1000, *A[:5], None) == WS
+
+
 def test_workspace_grows_with_sizes():
     d = _desc()
     small = lib.spd_attn_workspace_bytes(ctypes.byref(d), 4, 1000)
