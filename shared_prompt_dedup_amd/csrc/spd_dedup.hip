@@ -486,8 +486,13 @@ constexpr int kU = 4;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Output rows are written once and not re-read by this kernel: non-temporal.
+// Stores of output rows.  The [B, S, W] outputs of reconstruct and of the
+// backward of pack_rows (2.2 GB on the 32K-prompt batch) measured 8-10%
+// faster with plain stores; the [T, W] outputs of pack_rows and of the
+// backward of reconstruct (a seventh of that, written while reading the large
+// side) 10-12% faster with non-temporal ones, in the layer step.
 __device__ inline void stream_store(u32x4 *p, const u32x4 &v) { __builtin_nontemporal_store(v, p); }
+__device__ inline void plain_store(u32x4 *p, const u32x4 &v) { *p = v; }
 
 // Non-temporal loads for inputs read once from cold HBM (pack_rows' [B,S,W]
 // rows, reconstruct_bwd's gradient cells): measured 4% and 8% faster in the
@@ -506,8 +511,36 @@ __global__ void __launch_bounds__(kRowThreads) k_pack_rows(int64_t T, int64_t ve
                                                             u32x4 *__restrict__ packed) {
   const int lane = __lane_id();
   const int64_t nwaves = int64_t(gridDim.x) * (kRowThreads / 64);
-  for (int64_t j = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; j < T; j += nwaves) {
-    const int64_t r = cell_row ? cell_row[src[j]] : src[j];
+  const int64_t jfirst = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64;
+  auto row_of = [&](int64_t j) -> int64_t { return cell_row ? cell_row[src[j]] : src[j]; };
+  if (vec_per_row <= 64 * kU) {
+    // as in k_reconstruct: the next row's loads go out before this row's stores
+    u32x4 v[kU];
+    auto load = [&](int64_t j, u32x4 (&x)[kU]) {
+      const int64_t r = j < T ? row_of(j) : -1;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = u * 64 + lane;
+        x[u] = (c < vec_per_row && r >= 0) ? stream_load(rows + r * vec_per_row + c) : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    load(jfirst, v);
+    for (int64_t j = jfirst; j < T; j += nwaves) {
+      u32x4 vn[kU];
+      load(j + nwaves, vn);
+      u32x4 *out = packed + j * vec_per_row;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = u * 64 + lane;
+        if (c < vec_per_row) stream_store(out + c, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = vn[u];
+    }
+    return;
+  }
+  for (int64_t j = jfirst; j < T; j += nwaves) {
+    const int64_t r = row_of(j);
     const u32x4 *in = rows + r * vec_per_row;
     u32x4 *out = packed + j * vec_per_row;
     for (int64_t c0 = 0; c0 < vec_per_row; c0 += 64 * kU) {
@@ -541,13 +574,18 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
                                                               u32x4 *__restrict__ out) {
   const int lane = __lane_id();
   const int64_t nwaves = int64_t(gridDim.x) * (kRowThreads / 64);
-  for (int64_t j = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; j < T; j += nwaves) {
+  const int64_t jfirst = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64;
+  // The readers of packed row j: samples members[m0 .. m1) (every sample for a
+  // shared-prefix row; just b0 for a response row), column t.
+  auto readers = [&](int64_t j, int64_t &b0, int64_t &t, int &m0, int &m1, const int32_t *&members,
+                     bool &every_sample) {
     const int64_t s = plan.src[j];
-    const int64_t b0 = s / S;
-    const int64_t t = s - b0 * S;
-    int m0 = 0, m1 = 1;
-    const int32_t *members = nullptr;
-    bool every_sample = false;      // a shared-prefix row: read by every sample
+    b0 = s / S;
+    t = s - b0 * S;
+    m0 = 0;
+    m1 = 1;
+    members = nullptr;
+    every_sample = false;
     if (t < plan.counts[4]) {
       m1 = static_cast<int>(plan.B);
       every_sample = true;
@@ -557,23 +595,59 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
       m1 = plan.grp_off[g + 1];
       members = plan.grp_idx;
     }
-    const u32x4 *in = packed + j * vec_per_row;
-    for (int64_t c0 = 0; c0 < vec_per_row; c0 += 64 * kU) {
-      u32x4 v[kU];
+  };
+  auto store_row = [&](int64_t j, int64_t c0, const u32x4 (&v)[kU]) {
+    int64_t b0, t;
+    int m0, m1;
+    const int32_t *members;
+    bool every_sample;
+    readers(j, b0, t, m0, m1, members, every_sample);
+    for (int m = m0; m < m1; ++m) {
+      const int64_t b = every_sample ? m : (members ? members[m] : b0);
+      u32x4 *o = out + (b * S + t) * vec_per_row;
+      const bool zero = SOURCE_ONLY && b != b0;
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int64_t c = c0 + u * 64 + lane;
-        if (c < vec_per_row) v[u] = in[c];
+        if (c < vec_per_row) plain_store(o + c, zero ? u32x4{0u, 0u, 0u, 0u} : v[u]);
       }
-      for (int m = m0; m < m1; ++m) {
-        const int64_t b = every_sample ? m : (members ? members[m] : b0);
-        u32x4 *o = out + (b * S + t) * vec_per_row;
-        const bool zero = SOURCE_ONLY && b != b0;
+    }
+  };
+  if (vec_per_row <= 64 * kU) {
+    // One chunk covers a row: the next row's loads go out before this row's
+    // stores, so waiting for them (the memory counter is in order) does not
+    // wait for the stores.
+    u32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = u32x4{0u, 0u, 0u, 0u};
+    if (jfirst < T) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (u * 64 + lane < vec_per_row) v[u] = packed[jfirst * vec_per_row + u * 64 + lane];
+    }
+    for (int64_t j = jfirst; j < T; j += nwaves) {
+      const int64_t jn = j + nwaves;
+      u32x4 vn[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        vn[u] = u32x4{0u, 0u, 0u, 0u};
+        if (jn < T && u * 64 + lane < vec_per_row) vn[u] = packed[jn * vec_per_row + u * 64 + lane];
+      }
+      store_row(j, 0, v);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = vn[u];
+    }
+  } else {
+    for (int64_t j = jfirst; j < T; j += nwaves) {
+      const u32x4 *in = packed + j * vec_per_row;
+      for (int64_t c0 = 0; c0 < vec_per_row; c0 += 64 * kU) {
+        u32x4 v[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
           const int64_t c = c0 + u * 64 + lane;
-          if (c < vec_per_row) stream_store(o + c, zero ? u32x4{0u, 0u, 0u, 0u} : v[u]);
+          if (c < vec_per_row) v[u] = in[c];
         }
+        store_row(j, c0, v);
       }
     }
   }
@@ -583,7 +657,7 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
     for (int64_t r = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; r < cells; r += nwaves) {
       if (plan.dst[r] >= 0) continue;
       u32x4 *o = out + r * vec_per_row;
-      for (int64_t c = lane; c < vec_per_row; c += 64) stream_store(o + c, z);
+      for (int64_t c = lane; c < vec_per_row; c += 64) plain_store(o + c, z);
     }
   }
 }
