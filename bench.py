@@ -48,8 +48,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = None     # sources the figures below were taken with (None: none taken yet)
+TRAFFIC_SOURCES_SHA256 = "e0d4f649d612073a53aeb01b0617623587018df1b9360b97c23624d464d8756b"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
+    "long_2x8_p32768_r256to1024_unpad": {
+        "fwd": (1641693, 307966), "bwd_pre": (307996, 9784), "bwd_dq": (1806325, 303186),
+        "bwd_dkdv": (5377310, 303307), "reconstruct": (162724, 2162688), "pack_rows": (152795, 303191),
+        "reconstruct_bwd": (1070306, 303180), "pack_rows_bwd": (162557, 2162688),
+    },
 }
 
 
