@@ -652,12 +652,19 @@ __global__ void __launch_bounds__(kRowThreads) k_reconstruct(int64_t T, int64_t 
     }
   }
   if (plan.counts[2] != 0) {
+    // This wave's cells are r = w, w + nwaves, ...: lane l reads the map of
+    // the l-th of the next 64 at once, and the cells with none are zeroed.
     const int64_t cells = plan.B * S;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int64_t r = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; r < cells; r += nwaves) {
-      if (plan.dst[r] >= 0) continue;
-      u32x4 *o = out + r * vec_per_row;
-      for (int64_t c = lane; c < vec_per_row; c += 64) plain_store(o + c, z);
+    for (int64_t r0 = int64_t(blockIdx.x) * (kRowThreads / 64) + threadIdx.x / 64; r0 < cells; r0 += 64 * nwaves) {
+      const int64_t rl = r0 + lane * nwaves;
+      uint64_t todo = __ballot(rl < cells && plan.dst[rl] < 0);
+      while (todo) {
+        const int l = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        u32x4 *o = out + (r0 + int64_t(l) * nwaves) * vec_per_row;
+        for (int64_t c = lane; c < vec_per_row; c += 64) plain_store(o + c, z);
+      }
     }
   }
 }
