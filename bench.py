@@ -48,12 +48,12 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "e0d4f649d612073a53aeb01b0617623587018df1b9360b97c23624d464d8756b"
+TRAFFIC_SOURCES_SHA256 = "e4c7c9fd96f5599b85db278c4f757355d5b4313921c1b5b393696a8c8d402149"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
-        "fwd": (1641693, 307966), "bwd_pre": (307996, 9784), "bwd_dq": (1806325, 303186),
-        "bwd_dkdv": (5377310, 303307), "reconstruct": (162724, 2162688), "pack_rows": (152795, 303191),
-        "reconstruct_bwd": (1070306, 303180), "pack_rows_bwd": (162557, 2162688),
+        "fwd": (1641604, 307964), "bwd_pre": (307996, 9784), "bwd_dq": (1806701, 303183),
+        "bwd_dkdv": (5318286, 303337), "reconstruct": (163423, 2162688), "pack_rows": (152795, 303186),
+        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163193, 2162688),
     },
 }
 
