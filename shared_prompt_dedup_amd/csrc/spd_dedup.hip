@@ -262,42 +262,100 @@ __device__ inline bool mask_at(const void *mask, int esz, int64_t i) {
   return static_cast<const int64_t *>(mask)[i] != 0;
 }
 
-// Counts the kept tokens of [t0, t1) of one row (block-wide).
-__device__ inline int block_count_kept(const void *mask, int esz, int64_t row_base, int64_t t0, int64_t t1) {
-  int c = 0;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) c += mask_at(mask, esz, row_base + t);
-  __shared__ int part[4];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
-  __syncthreads();
-  if (__lane_id() == 0) part[threadIdx.x / 64] = c;
-  __syncthreads();
-  return part[0] + part[1] + part[2] + part[3];
+// Padded packing (every column kept): segment lengths from the shapes alone.
+__global__ void k_seg_lengths_dense(int64_t S, int64_t P, spd_plan plan) {
+  const int64_t L0 = plan.counts[4];
+  for (int b = threadIdx.x; b < plan.B; b += blockDim.x) {
+    const int g = plan.group_of[b];
+    plan.resp_len[b] = static_cast<int>(S - P);
+    if (plan.rep[g] == b) plan.prompt_len[g] = static_cast<int>(P - L0);
+    if (plan.rep[0] == b) plan.counts[5] = static_cast<int>(L0);
+  }
 }
 
-// One block per sample: kept response tokens, and the kept prompt tokens of
-// its group when the sample is the group's first member.
-__global__ void __launch_bounds__(256) k_seg_lengths(int64_t S, int64_t P, const void *mask, int esz,
-                                                      int unpad, spd_plan plan) {
-  const int b = blockIdx.x;
-  const int g = plan.group_of[b];
-  const bool first = plan.rep[g] == b;
-  const bool first_of_all = plan.rep[0] == b;    // packs the shared prefix, if any
-  const int64_t L0 = plan.counts[4];
-  int r, p = 0, lp = 0;
-  if (unpad) {
-    r = block_count_kept(mask, esz, int64_t(b) * S, P, S);
-    if (first) p = block_count_kept(mask, esz, int64_t(b) * S, L0, P);
-    if (first_of_all && L0 > 0) lp = block_count_kept(mask, esz, int64_t(b) * S, 0, L0);
-  } else {
-    r = static_cast<int>(S - P);
-    p = static_cast<int>(P - L0);
-    lp = static_cast<int>(L0);
+// Unpadded packing works on chunks of kPackChunk columns of each sample's row,
+// one block per (sample, chunk), each thread kPackPer consecutive columns.  A
+// row's columns fall in three parts: the shared prefix [0, L0), the prompt
+// [L0, P) and the response [P, S).  k_chunk_counts counts the kept columns
+// of every (sample, chunk, part); k_chunk_bases turns them into exclusive
+// scans over each (sample, part)'s chunks and the part totals into segment
+// lengths; k_scatter_chunks then gives a kept column the rank of its chunk's
+// base plus its rank inside the chunk.
+constexpr int kPackChunk = 1024;
+constexpr int kPackPer = kPackChunk / 256;
+
+__device__ inline int pack_part(int64_t t, int64_t L0, int64_t P) { return t < L0 ? 0 : (t < P ? 1 : 2); }
+
+// Sums of three per-thread values over a 256-thread block (red: 12 ints).
+__device__ inline void block_sum3(int &v0, int &v1, int &v2, int *red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    v0 += __shfl_xor(v0, off, 64);
+    v1 += __shfl_xor(v1, off, 64);
+    v2 += __shfl_xor(v2, off, 64);
   }
-  if (threadIdx.x == 0) {
-    plan.resp_len[b] = r;
-    if (first) plan.prompt_len[g] = p;
-    if (first_of_all) plan.counts[5] = lp;
+  const int w = threadIdx.x / 64;
+  __syncthreads();
+  if (__lane_id() == 0) {
+    red[3 * w] = v0;
+    red[3 * w + 1] = v1;
+    red[3 * w + 2] = v2;
+  }
+  __syncthreads();
+  v0 = red[0] + red[3] + red[6] + red[9];
+  v1 = red[1] + red[4] + red[7] + red[10];
+  v2 = red[2] + red[5] + red[8] + red[11];
+}
+
+// cnt[(b * nch + c) * 3 + part]: kept columns of sample b's own row in chunk c.
+__global__ void __launch_bounds__(256) k_chunk_counts(int64_t S, int64_t P, const void *mask, int esz, int nch,
+                                                       spd_plan plan, int32_t *__restrict__ cnt) {
+  __shared__ int red[12];
+  const int b = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int64_t L0 = plan.counts[4];
+  const int64_t t0 = int64_t(c) * kPackChunk + int64_t(threadIdx.x) * kPackPer;
+  int v0 = 0, v1 = 0, v2 = 0;
+#pragma unroll
+  for (int i = 0; i < kPackPer; ++i) {
+    const int64_t t = t0 + i;
+    if (t < S) {
+      const int k = mask_at(mask, esz, int64_t(b) * S + t) ? 1 : 0;
+      const int part = pack_part(t, L0, P);
+      v0 += part == 0 ? k : 0;
+      v1 += part == 1 ? k : 0;
+      v2 += part == 2 ? k : 0;
+    }
+  }
+  block_sum3(v0, v1, v2, red);
+  if (threadIdx.x < 3) cnt[(int64_t(b) * nch + c) * 3 + threadIdx.x] = threadIdx.x == 0 ? v0 : (threadIdx.x == 1 ? v1 : v2);
+}
+
+// One wave per (sample, part): cnt becomes the exclusive scan over the
+// chunks of that sample's part; the totals give resp_len (every sample),
+// prompt_len (a group's first member) and counts[5], the shared prefix's kept
+// length (the first group's first member).
+__global__ void __launch_bounds__(256) k_chunk_bases(int nch, spd_plan plan, int32_t *__restrict__ cnt) {
+  const int pair = blockIdx.x * 4 + threadIdx.x / 64;
+  if (pair >= 3 * plan.B) return;
+  const int lane = __lane_id();
+  const int b = pair / 3, part = pair % 3;
+  int32_t *run = cnt + int64_t(b) * nch * 3 + part;
+  int total = 0;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
+    const int x = c < nch ? run[3 * int64_t(c)] : 0;
+    const int inc = wave_inclusive_scan(x);
+    if (c < nch) run[3 * int64_t(c)] = total + inc - x;
+    total += __shfl(inc, 63, 64);
+  }
+  if (lane != 0) return;
+  if (part == 2) {
+    plan.resp_len[b] = total;
+  } else if (part == 1) {
+    const int g = plan.group_of[b];
+    if (plan.rep[g] == b) plan.prompt_len[g] = total;
+  } else if (plan.rep[0] == b) {
+    plan.counts[5] = total;
   }
 }
 
@@ -337,39 +395,78 @@ __global__ void __launch_bounds__(kFinalThreads) k_seg_offsets(int B, int32_t *_
   }
 }
 
-// Walks columns [t0, t1) of a row in order, 256 at a time, giving each kept
-// column its rank among the kept columns (ballot + popcount per wave).
-template <typename F>
-__device__ inline void for_kept_columns(const void *mask, int esz, int unpad, int64_t mask_row, int64_t t0,
-                                        int64_t t1, F &&fn) {
-  __shared__ int wave_cnt[4];
-  int running = 0;
-  const int wid = threadIdx.x / 64;
-  const uint64_t lt = (uint64_t(1) << __lane_id()) - 1;
-  for (int64_t c0 = t0; c0 < t1; c0 += blockDim.x) {
-    const int64_t t = c0 + threadIdx.x;
-    const bool in = t < t1;
-    const bool kept = in && (!unpad || mask_at(mask, esz, mask_row + t));
-    const uint64_t bal = __ballot(kept);
-    __syncthreads();
-    if (__lane_id() == 0) wave_cnt[wid] = __popcll(bal);
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int w = 0; w < 4; ++w) {
-      before += (w < wid) ? wave_cnt[w] : 0;
-      total += wave_cnt[w];
+// Unpadded scatter, one block per (sample b, chunk c): dst for every (b, t)
+// of the chunk; src, seg_start, dedup ids and positions for the packed rows
+// b owns there (its response, its group's prompt when it is the first member,
+// the shared prefix when it is the first group's first member).  A part's
+// kept-ness comes from the row it is packed from: the prefix from the first
+// group's first member, the prompt from the group's first member, the
+// response from b.
+__global__ void __launch_bounds__(256) k_scatter_chunks(int64_t S, int64_t P, const int64_t *__restrict__ ids,
+                                                         const int64_t *__restrict__ pos, const void *mask, int esz,
+                                                         int nch, spd_plan plan, const int32_t *__restrict__ cnt,
+                                                         int64_t *__restrict__ dids, int64_t *__restrict__ dpos) {
+  __shared__ int scan_tmp[4];
+  const int b = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int g = plan.group_of[b];
+  const int from0 = plan.rep[0], from1 = plan.rep[g];
+  const int seg1 = plan.prompt_off[g], seg2 = plan.resp_off[b];
+  const int64_t L0 = plan.counts[4];
+  const int64_t t0 = int64_t(c) * kPackChunk + int64_t(threadIdx.x) * kPackPer;
+  unsigned kept = 0;
+  int n0 = 0, n1 = 0, n2 = 0;
+#pragma unroll
+  for (int i = 0; i < kPackPer; ++i) {
+    const int64_t t = t0 + i;
+    if (t < S) {
+      const int part = pack_part(t, L0, P);
+      const int from = part == 0 ? from0 : (part == 1 ? from1 : b);
+      const int k = mask_at(mask, esz, int64_t(from) * S + t) ? 1 : 0;
+      kept |= unsigned(k) << i;
+      n0 += part == 0 ? k : 0;
+      n1 += part == 1 ? k : 0;
+      n2 += part == 2 ? k : 0;
     }
-    if (in) fn(t, kept, running + before + __popcll(bal & lt));
-    running += total;
   }
+  int tot;
+  // rank in the part = the chunk's base in the row the part comes from + kept
+  // columns of the part before this one in the chunk
+  int r0 = block_exclusive_scan(n0, scan_tmp, tot) + cnt[(int64_t(from0) * nch + c) * 3];
+  __syncthreads();
+  int r1 = block_exclusive_scan(n1, scan_tmp, tot) + cnt[(int64_t(from1) * nch + c) * 3 + 1];
+  __syncthreads();
+  int r2 = block_exclusive_scan(n2, scan_tmp, tot) + cnt[(int64_t(b) * nch + c) * 3 + 2];
+  int pads = 0;
+#pragma unroll
+  for (int i = 0; i < kPackPer; ++i) {
+    const int64_t t = t0 + i;
+    if (t < S) {
+      const int part = pack_part(t, L0, P);
+      const int64_t cell = int64_t(b) * S + t;
+      if ((kept >> i) & 1) {
+        const int rank = part == 0 ? r0++ : (part == 1 ? r1++ : r2++);
+        const int seg = part == 0 ? 0 : (part == 1 ? seg1 : seg2);
+        const int j = seg + rank;
+        plan.dst[cell] = j;
+        if (b == (part == 0 ? from0 : (part == 1 ? from1 : b))) {
+          plan.src[j] = static_cast<int32_t>(cell);
+          plan.seg_start[j] = seg;
+          dids[j] = ids[cell];
+          dpos[j] = pos[cell];
+        }
+      } else {
+        plan.dst[cell] = -1;
+        ++pads;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) pads += __shfl_xor(pads, off, 64);
+  if (__lane_id() == 0 && pads) atomicAdd(&plan.counts[2], pads);
 }
 
-// One block per sample: dst for every (b, t); src, seg_start, dedup ids and
-// positions for the packed rows this sample owns (its response, and its
-// group's prompt when it is the first member).
 // Padded format (every column kept): a column's packed row is its offset in
-// its segment, so one thread per batch cell, no scan.  Same results as
-// k_scatter with unpad = 0.
+// its segment, so one thread per batch cell, no scan.
 __global__ void __launch_bounds__(256) k_scatter_dense(int64_t S, int64_t P, const int64_t *__restrict__ ids,
                                                         const int64_t *__restrict__ pos, const void *mask, int esz,
                                                         spd_plan plan, int64_t *__restrict__ dids,
@@ -406,72 +503,6 @@ __global__ void __launch_bounds__(256) k_scatter_dense(int64_t S, int64_t P, con
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) kept_pads += __shfl_xor(kept_pads, off, 64);
-  if (__lane_id() == 0 && kept_pads) atomicAdd(&plan.counts[3], kept_pads);
-}
-
-__global__ void __launch_bounds__(256) k_scatter(int64_t S, int64_t P, const int64_t *__restrict__ ids,
-                                                  const int64_t *__restrict__ pos, const void *mask, int esz,
-                                                  int unpad, spd_plan plan, int64_t *__restrict__ dids,
-                                                  int64_t *__restrict__ dpos) {
-  const int b = blockIdx.x;
-  const int g = plan.group_of[b];
-  const int r = plan.rep[g];
-  const int po = plan.prompt_off[g];
-  const int ro = plan.resp_off[b];
-  int pads = 0;       // (b, t) mapped to no packed row (unpad mode)
-  int kept_pads = 0;  // packed rows whose mask entry is 0 (padded mode with a mask)
-  const bool count_kept_pads = !unpad && mask;
-  // shared prefix columns [0, L0): packed once, from the first sample of the
-  // first group, ahead of every group
-  const int64_t L0 = plan.counts[4];
-  if (L0 > 0) {
-    const int r0 = plan.rep[0];
-    for_kept_columns(mask, esz, unpad, int64_t(r0) * S, 0, L0, [&](int64_t t, bool kept, int rank) {
-      plan.dst[int64_t(b) * S + t] = kept ? rank : -1;
-      pads += !kept;
-      if (kept && b == r0) {
-        const int64_t s = int64_t(r0) * S + t;
-        plan.src[rank] = static_cast<int32_t>(s);
-        plan.seg_start[rank] = 0;
-        dids[rank] = ids[s];
-        dpos[rank] = pos[s];
-        if (count_kept_pads) kept_pads += !mask_at(mask, esz, s);
-      }
-    });
-  }
-  // prompt columns [L0, P): kept-ness and positions come from the first member
-  for_kept_columns(mask, esz, unpad, int64_t(r) * S, L0, P, [&](int64_t t, bool kept, int rank) {
-    const int j = po + rank;
-    plan.dst[int64_t(b) * S + t] = kept ? j : -1;
-    pads += !kept;
-    if (kept && b == r) {
-      const int64_t s = int64_t(r) * S + t;
-      plan.src[j] = static_cast<int32_t>(s);
-      plan.seg_start[j] = po;
-      dids[j] = ids[s];
-      dpos[j] = pos[s];
-      if (count_kept_pads) kept_pads += !mask_at(mask, esz, s);
-    }
-  });
-  for_kept_columns(mask, esz, unpad, int64_t(b) * S, P, S, [&](int64_t t, bool kept, int rank) {
-    const int j = ro + rank;
-    const int64_t s = int64_t(b) * S + t;
-    plan.dst[s] = kept ? j : -1;
-    pads += !kept;
-    if (kept) {
-      plan.src[j] = static_cast<int32_t>(s);
-      plan.seg_start[j] = ro;
-      dids[j] = ids[s];
-      dpos[j] = pos[s];
-      if (count_kept_pads) kept_pads += !mask_at(mask, esz, s);
-    }
-  });
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    pads += __shfl_xor(pads, off, 64);
-    kept_pads += __shfl_xor(kept_pads, off, 64);
-  }
-  if (__lane_id() == 0 && pads) atomicAdd(&plan.counts[2], pads);
   if (__lane_id() == 0 && kept_pads) atomicAdd(&plan.counts[3], kept_pads);
 }
 
@@ -860,10 +891,12 @@ extern "C" spd_status spd_group(const int64_t *input_ids, int64_t B, int64_t S, 
   return SPD_OK;
 }
 
+// seg: 2 B ints (the segment-offset scan); cnt: 3 ints per (sample, chunk).
+static int64_t pack_chunks(int64_t S) { return (S + kPackChunk - 1) / kPackChunk; }
+
 extern "C" size_t spd_pack_workspace_bytes(int64_t B, int64_t S) {
-  (void)S;
-  if (B < 1) return 0;
-  return round_up(size_t(2 * B) * 4, 256);
+  if (B < 1 || S < 1) return 0;
+  return round_up(size_t(2 * B) * 4, 256) + round_up(size_t(B) * size_t(pack_chunks(S)) * 3 * 4, 256);
 }
 
 extern "C" spd_status spd_pack(const int64_t *input_ids, const int64_t *position_ids, const void *attention_mask,
@@ -885,13 +918,24 @@ extern "C" spd_status spd_pack(const int64_t *input_ids, const int64_t *position
   int32_t *seg = static_cast<int32_t *>(workspace);
   // padded format with a mask: pads may sit among the packed rows, which the attention calls must not see
   plan->padded_with_mask = (!use_unpad && attention_mask) ? 1 : 0;
-  hipLaunchKernelGGL(k_seg_lengths, dim3(B), dim3(256), 0, st, S, P, attention_mask, esz, use_unpad, *plan);
+  const int nch = static_cast<int>(pack_chunks(S));
+  int32_t *cnt = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + round_up(size_t(2 * B) * 4, 256));
+  const unsigned chunk_blocks = static_cast<unsigned>(B * nch);
+  if (use_unpad) {
+    hipLaunchKernelGGL(k_chunk_counts, dim3(chunk_blocks), dim3(256), 0, st, S, P, attention_mask, esz, nch, *plan,
+                       cnt);
+    SPD_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_chunk_bases, dim3(static_cast<unsigned>((3 * B + 3) / 4)), dim3(256), 0, st, nch, *plan,
+                       cnt);
+  } else {
+    hipLaunchKernelGGL(k_seg_lengths_dense, dim3(1), dim3(256), 0, st, S, P, *plan);
+  }
   SPD_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_seg_offsets, dim3(1), dim3(kFinalThreads), 0, st, int(B), seg, *plan);
   SPD_LAUNCH_CHECK();
   if (use_unpad)
-    hipLaunchKernelGGL(k_scatter, dim3(B), dim3(256), 0, st, S, P, input_ids, position_ids, attention_mask, esz,
-                       use_unpad, *plan, dedup_ids, dedup_pos);
+    hipLaunchKernelGGL(k_scatter_chunks, dim3(chunk_blocks), dim3(256), 0, st, S, P, input_ids, position_ids,
+                       attention_mask, esz, nch, *plan, cnt, dedup_ids, dedup_pos);
   else
     hipLaunchKernelGGL(k_scatter_dense, dim3(unsigned(std::min<int64_t>((B * S + 255) / 256, 65536))), dim3(256),
                        0, st, S, P, input_ids, position_ids, attention_mask, esz, *plan, dedup_ids, dedup_pos);
