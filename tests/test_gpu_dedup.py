@@ -126,6 +126,43 @@ def test_grouping_across_hash_chunks(S, R):
     assert oinfo["G"] == 8          # {0, 2, 6} and {3, 8} group; the other six rows stand alone
 
 
+def _holey_batch(P, R, G, n, seed, prefix=0):
+    """G groups of n samples (members interleaved): prompts identical within a
+    group, with left pads and random holes in the prompt mask (the same for every
+    member); responses of random tokens with random holes.  With prefix > 0,
+    every prompt starts with the same prefix tokens and prefix mask."""
+    from workloads import Batch
+    rng = np.random.default_rng(seed)
+    S, B = P + R, G * n
+    prompts = rng.integers(1, 1000, size=(G, P))
+    pmask = (rng.random((G, P)) > 0.2).astype(np.int64)
+    pmask[:, :37] = 0
+    if prefix:
+        prompts[:, :prefix] = prompts[0, :prefix]
+        pmask[:, :prefix] = pmask[0, :prefix]
+    order = rng.permutation(B)
+    ids = np.zeros((B, S), dtype=np.int64)
+    mask = np.zeros((B, S), dtype=np.int64)
+    for b in range(B):
+        g = order[b] % G
+        ids[b, :P], mask[b, :P] = prompts[g], pmask[g]
+        ids[b, P:] = rng.integers(1, 1000, size=R)
+        mask[b, P:] = rng.random(R) > 0.3
+    pos = np.maximum(np.cumsum(mask, axis=1) - 1, 0).astype(np.int64)
+    return Batch(ids, pos, mask, R, None, None)
+
+
+@pytest.mark.parametrize("P,R", [(2500, 1500), (1023, 1026), (3072, 5)], ids=["mid_chunk", "edge_chunk", "aligned"])
+def test_unpad_pack_across_column_chunks(P, R):
+    """Unpadded packing counts kept columns per column chunk of each row: the
+    prompt/response boundary inside a chunk, one column before a chunk
+    boundary, and on one; masks with holes in prompts and responses."""
+    bt = _holey_batch(P, R, 3, 3, seed=P + R)
+    say(f"[dedup plan] unpad across column chunks P={P} R={R}")
+    oinfo, _ = _check_plan(bt, True)
+    assert oinfo["G"] == 3 and 0 < oinfo["T"] < bt.input_ids.size
+
+
 def test_maximum_batch_size():
     """B = 65,536 rows, the largest batch the C ABI takes, of 3-token prompts over a
     3-token vocabulary: all 27 prompts occur, each group with thousands of members."""

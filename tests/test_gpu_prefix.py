@@ -70,6 +70,27 @@ def test_prefix_plan_bit_exact(w):
         np.testing.assert_array_equal(getattr(p, f)[:T].cpu().numpy(), oinfo[f], err_msg=f)
 
 
+@pytest.mark.parametrize("L0,P,R", [(1500, 2600, 900), (1024, 1300, 2000)], ids=["prefix_mid_chunk", "prefix_aligned"])
+def test_prefix_plan_across_column_chunks(L0, P, R):
+    """The shared prefix, the group prompts and the responses packed from
+    masks with holes, with the prefix's end inside a column chunk or on its
+    boundary: plans bit-exact with the oracle."""
+    from test_gpu_dedup import _holey_batch
+    bt = _holey_batch(P, R, 3, 2, seed=L0 + P, prefix=L0)
+    say(f"[prefix] plan across column chunks L0={L0} P={P}")
+    (odids, odpos, oinfo), (gdids, gdpos, ginfo), _ = _plans(bt, True)
+    assert oinfo["L0"] >= L0 and ginfo["L0"] == oinfo["L0"] and ginfo["T"] == oinfo["T"]
+    np.testing.assert_array_equal(gdids.cpu().numpy(), odids)
+    np.testing.assert_array_equal(gdpos.cpu().numpy(), odpos)
+    p, G, T = ginfo.plan, oinfo["G"], oinfo["T"]
+    for f in ("prompt_off", "prompt_len", "rep"):
+        np.testing.assert_array_equal(getattr(p, f)[:G].cpu().numpy(), oinfo[f], err_msg=f)
+    for f in ("group_of", "resp_off", "resp_len", "dst"):
+        np.testing.assert_array_equal(getattr(p, f).cpu().numpy(), oinfo[f], err_msg=f)
+    for f in ("src", "seg_start"):
+        np.testing.assert_array_equal(getattr(p, f)[:T].cpu().numpy(), oinfo[f], err_msg=f)
+
+
 @pytest.mark.parametrize("w", PLAN_CASES[:2] + PLAN_CASES[-1:], ids=[w.name for w in PLAN_CASES[:2] + PLAN_CASES[-1:]])
 def test_prefix_rows(w):
     import shared_prompt_dedup_amd as spd
