@@ -48,12 +48,12 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "e4c7c9fd96f5599b85db278c4f757355d5b4313921c1b5b393696a8c8d402149"
+TRAFFIC_SOURCES_SHA256 = "c8063a8582ac3d8d86603d0b691bbf44780d9df8ebc74a5d23535cd029617de3"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
-        "fwd": (1641604, 307964), "bwd_pre": (307996, 9784), "bwd_dq": (1806701, 303183),
-        "bwd_dkdv": (5318286, 303337), "reconstruct": (163423, 2162688), "pack_rows": (152795, 303186),
-        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163193, 2162688),
+        "fwd": (1641946, 307966), "bwd_pre": (307995, 9784), "bwd_dq": (1805538, 303184),
+        "bwd_dkdv": (5448323, 303258), "reconstruct": (163482, 2162688), "pack_rows": (152799, 303192),
+        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163206, 2162688),
     },
 }
 
