@@ -135,7 +135,12 @@ spd_status spd_group(const int64_t *input_ids, int64_t B, int64_t S, int64_t res
 
 /* ----------------------------------------------------------------- packing */
 
-/* Workspace bytes spd_pack needs. */
+/*
+ * Workspace bytes spd_pack needs (device memory, caller-owned, any contents):
+ * 2 B int32 for the segment-offset scan plus 3 int32 per 1024 columns of every
+ * row for the unpadded pack's per-chunk kept counts, each part rounded up to
+ * 256 bytes.  0 when B < 1 or S < 1.
+ */
 size_t spd_pack_workspace_bytes(int64_t B, int64_t S);
 
 /*

@@ -74,6 +74,14 @@ def test_group_rejects_bad_arguments():
     assert lib.spd_group(A[12], 65536, 40000, 1000, ctypes.byref(big), None, A[13], 1 << 40, None) == UNSUPPORTED
 
 
+def test_pack_workspace_size():
+    r = lambda x: (x + 255) // 256 * 256
+    assert lib.spd_pack_workspace_bytes(0, 8) == 0 and lib.spd_pack_workspace_bytes(4, 0) == 0
+    for B, S in ((4, 8), (16, 33792), (1, 1024), (1, 1025), (65536, 32)):
+        chunks = (S + 1023) // 1024
+        assert lib.spd_pack_workspace_bytes(B, S) == r(2 * B * 4) + r(B * chunks * 3 * 4), (B, S)
+
+
 def test_pack_rejects_bad_arguments():
     ws = lib.spd_pack_workspace_bytes(4, 8)
     p = _plan()
