@@ -48,12 +48,12 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "c8063a8582ac3d8d86603d0b691bbf44780d9df8ebc74a5d23535cd029617de3"
+TRAFFIC_SOURCES_SHA256 = "481cc7d30647f0d31aab2fd1dd0aa99d378d26033b8ee8cb804442b0b5961250"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
-        "fwd": (1641946, 307966), "bwd_pre": (307995, 9784), "bwd_dq": (1805538, 303184),
-        "bwd_dkdv": (5448323, 303258), "reconstruct": (163482, 2162688), "pack_rows": (152799, 303192),
-        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163206, 2162688),
+        "fwd": (1642404, 307968), "bwd_pre": (307997, 9784), "bwd_dq": (1805100, 303188),
+        "bwd_dkdv": (5233348, 303225), "reconstruct": (163468, 2162688), "pack_rows": (152799, 303191),
+        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163235, 2162688),
     },
 }
 

@@ -108,12 +108,24 @@ __device__ inline int swz_off(int row, int chunk) {
 // inline assembly: the compiler, seeing an LDS DMA, would otherwise make every
 // later transposing LDS read wait for all outstanding vector loads, including
 // the prefetches of later stages.  Callers wait for completion themselves
-// (wait_ring) before a barrier publishes the data.  The s_nop is the
-// wait state an LDS DMA needs after M0 is written.
+// (wait_ring) before a barrier publishes the data.
+//
+// The compiler does not know that the assembly holds a vector-memory load, so
+// it pads none of that load's wait states.  A vector-memory instruction must
+// come at least 5 wait states after a VALU write of an SGPR it reads, and the
+// compiler may produce base or M0 with one (v_readlane when it reloads a
+// spilled SGPR, v_readfirstlane): the load would then read a stale address.
+// The assembly therefore copies both with scalar moves, whose reads of a
+// VALU-written SGPR are interlocked and whose results a load may read at once;
+// the s_nop is the one wait state an LDS DMA needs after M0 is written.
 __device__ inline void dma16(const void *base, unsigned voff, const char *lds) {
   const unsigned m = __builtin_amdgcn_readfirstlane(
       static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)(lds))));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m) : "memory");
+  const void *b;
+  asm volatile("s_mov_b64 %0, %2\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0"
+               : "=&s"(b)
+               : "v"(voff), "s"(base), "s"(m)
+               : "memory", "m0");
 }
 
 // Direct-to-LDS copy of rows [r0, r0 + ROWS) of a [*, H, D] bf16 tensor (head
