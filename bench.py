@@ -48,12 +48,12 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "481cc7d30647f0d31aab2fd1dd0aa99d378d26033b8ee8cb804442b0b5961250"
+TRAFFIC_SOURCES_SHA256 = "6e8fb2daf03226c9427c5e58f816f68ac7773e1ba26d37e75249355d4a540cfa"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
-        "fwd": (1642404, 307968), "bwd_pre": (307997, 9784), "bwd_dq": (1805100, 303188),
-        "bwd_dkdv": (5233348, 303225), "reconstruct": (163468, 2162688), "pack_rows": (152799, 303191),
-        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163235, 2162688),
+        "fwd": (1641327, 307966), "bwd_pre": (307994, 9784), "bwd_dq": (1805210, 303188),
+        "bwd_dkdv": (5230649, 303233), "reconstruct": (163416, 2162688), "pack_rows": (152799, 303189),
+        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163180, 2162688),
     },
 }
 

@@ -390,11 +390,19 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
     if (wave == 1) dma_scalars(st + 2 * TB + 256, Dbuf + int64_t(h) * Tp + qb, lane);
   };
 
+  // Waves w and w + NW / 2 share a SIMD, and at equal priority issue goes to
+  // the older: wave w would take every matrix-core slot it can use, finish the
+  // block first and wait at the barrier while its partner ran alone.  So the
+  // older wave leads the block's first 32-row half (priority 2 over its
+  // partner's 1) and yields in the second (0).
+  const bool older = wave < NW / 2;
+  if (!older) set_prio<1>();
   for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
   for (int i = 0; i < n; ++i) {
     // waves 0-1 issue one extra load per block: waiting for PER-sized stages
     // only makes them wait longer, never too little
     wait_ring<STAGES, PER>(i, n);
+    if (older) set_prio<2>();
     if (i + STAGES - 1 < n) issue(i + STAGES - 1);
     int h, qb, qend;
     bool masked;
@@ -406,6 +414,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
     const char *sD = Qs + 2 * TB + 256;  // D
 #pragma unroll
     for (int m = 0; m < QB / 32; ++m) {
+      if (m == 1 && older) set_prio<0>();
       const int row0 = qb + 32 * m;
       if (row0 >= qend || (masked && row0 + 31 < kmin)) continue;
       const char *Qm = Qs + 32 * m * D * 2;

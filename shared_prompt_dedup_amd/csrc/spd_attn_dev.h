@@ -213,6 +213,15 @@ __device__ inline void wait_ring(int i, int n) {
 // the condition holds instead of being turned into selects on every pass.
 __device__ inline void keep_branch() { asm volatile(""); }
 
+// Sets this wave's issue priority, pinned in place: no instruction is
+// scheduled across the change.
+template <int P>
+__device__ inline void set_prio() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(P);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Instruction classes of the scheduler's group barriers.
