@@ -48,12 +48,12 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "6e8fb2daf03226c9427c5e58f816f68ac7773e1ba26d37e75249355d4a540cfa"
+TRAFFIC_SOURCES_SHA256 = "74fb05afd9ae4850010816703af2f550491b7dc39d2f7ec2d1175ce666e33b68"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
-        "fwd": (1641327, 307966), "bwd_pre": (307994, 9784), "bwd_dq": (1805210, 303188),
-        "bwd_dkdv": (5230649, 303233), "reconstruct": (163416, 2162688), "pack_rows": (152799, 303189),
-        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163180, 2162688),
+        "fwd": (1640152, 307972), "bwd_pre": (307992, 9784), "bwd_dq": (1805154, 303185),
+        "bwd_dkdv": (5196240, 303224), "reconstruct": (163418, 2162688), "pack_rows": (152799, 303188),
+        "reconstruct_bwd": (1070313, 303180), "pack_rows_bwd": (163258, 2162688),
     },
 }
 

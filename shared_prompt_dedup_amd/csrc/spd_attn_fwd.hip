@@ -11,8 +11,9 @@
 //
 // Block: 8 waves (two per SIMD, so one wave's MFMAs overlap the other's
 // softmax); wave w owns 32 query rows of one query head.  Per 64-key tile:
-// K and V are copied to LDS by direct-to-LDS loads (double buffered, one
-// barrier per tile), S^T = K Q^T puts one query per lane column so the row
+// K and V are copied to LDS by direct-to-LDS loads (a pair of tiles is read
+// while the next pair loads, one barrier per pair), S^T = K Q^T puts one
+// query per lane column so the row
 // statistics are per-lane scalars, and O^T = V^T P^T reads V^T with
 // transposing LDS reads.  The running maximum moves only when a tile exceeds
 // it by more than 2^8 (numerator and denominator share the reference, so this
@@ -40,9 +41,8 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
   constexpr int WPH = NW / HPW;          // waves per query head
   constexpr int KS = D / 16;             // contraction steps over head_dim
   constexpr int TB = BN * D * 2;         // bytes of one K or V tile
-  constexpr int STAGES = 3;              // tiles in flight: the ring hides two tiles of load latency
-  constexpr int PER = 2 * (BN * D / 8) / (NW * 64);   // direct-to-LDS loads per wave per tile
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * 2 * TB];   // [stage][K | V]
+  constexpr int SLOTS = 4;               // 64-key slots: the pair of tiles being read, the pair loading
+  __shared__ __attribute__((aligned(1024))) char smem[SLOTS * 2 * TB];   // [slot][K | V]
 
   const int tile_rank = blockIdx.x / HG;
   if (tile_rank >= *ntiles) return;
@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
   auto kt_of = [&](int i) { return i < nA ? i * BN : t.s0 + (i - nA) * BN; };
 
   auto issue = [&](int i) {
-    char *st = smem + (i % STAGES) * 2 * TB;
+    char *st = smem + (i % SLOTS) * 2 * TB;
     if (i < nA) {
       dma_rows2<BN, D, NW>(st, k, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
       dma_rows2<BN, D, NW>(st + TB, v, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
@@ -113,73 +113,91 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
     }
   };
   wait_vm_all();
-  for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
+  for (int i = 0; i < 2 && i < n; ++i) issue(i);
 
-  for (int i = 0; i < n; ++i) {
-    wait_ring<STAGES, PER>(i, n);
-    if (i + STAGES - 1 < n) issue(i + STAGES - 1);
-    const int kt = kt_of(i);
-    const bool phaseA = i < nA;
-    if (qlast < qw0 || (!phaseA && kt > qlast)) continue;   // nothing this wave can see
-    const char *Ks = smem + (i % STAGES) * 2 * TB;
-    const char *Vs = Ks + TB;
-    const bool need_mask = phaseA ? (kt + BN > lenA) : (kt + BN - 1 > qw0 || kt < seg_hi);
+  // One barrier per pair of tiles: past it, the pair's loads (issued a pair
+  // ahead) have landed for every wave, and every wave is done with the
+  // previous pair, whose slots then take the next one.  Waves w and w + NW/2
+  // share a SIMD; at equal priority issue goes to the older, which would take
+  // every matrix-core slot it can use and then wait at the barrier while its
+  // partner ran alone.  So the older wave leads the pair's first tile
+  // (priority 2 over its partner's 1) and yields in the second (0).
+  const bool older = wave < NW / 2;
+  if (!older) set_prio<1>();
+  for (int j = 0; j < (n + 1) / 2; ++j) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (older) set_prio<2>();
+    if (2 * j + 2 < n) issue(2 * j + 2);
+    if (2 * j + 3 < n) issue(2 * j + 3);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * j + u;
+      if (u == 1 && older) set_prio<0>();
+      if (i >= n) break;
+      const int kt = kt_of(i);
+      const bool phaseA = i < nA;
+      if (qlast < qw0 || (!phaseA && kt > qlast)) continue;   // nothing this wave can see
+      const char *Ks = smem + (i % SLOTS) * 2 * TB;
+      const char *Vs = Ks + TB;
+      const bool need_mask = phaseA ? (kt + BN > lenA) : (kt + BN - 1 > qw0 || kt < seg_hi);
 
-    f32x16 s[2];
+      f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[kb] = mfma(ld_lds8(Ks + koff[ks] + kb * 32 * D * 2), qf[ks], s[kb]);
-    }
-    sched_reads_ahead<kReadsAhead, 2 * KS, 1>();
-    if (need_mask) {
-      keep_branch();
+        for (int ks = 0; ks < KS; ++ks) s[kb] = mfma(ld_lds8(Ks + koff[ks] + kb * 32 * D * 2), qf[ks], s[kb]);
+      }
+      sched_reads_ahead<kReadsAhead, 2 * KS, 1>();
+      if (need_mask) {
+        keep_branch();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt + 32 * kb + c_row(r, half);
+            const bool vis = phaseA ? (key < lenA) : (key <= qrow && key >= seg_q);
+            s[kb][r] = vis ? s[kb][r] : -INFINITY;
+          }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float mn = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d) oacc[d] *= alpha;
+        m_run = mn;
+      }
+      bf16x8 pf[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt + 32 * kb + c_row(r, half);
-          const bool vis = phaseA ? (key < lenA) : (key <= qrow && key >= seg_q);
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -m_run));
+          l_run += p;
+          pf[2 * kb + (r >> 3)][r & 7] = static_cast<__bf16>(p);
         }
+      const char *vb[D / 32][2];
+#pragma unroll
+      for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) vb[dblk][w] = opaque_lds(Vs + voff[dblk][w]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int dblk = 0; dblk < D / 32; ++dblk) {
+          const bf16x8 a = ld_lds_tr_pair(vb[dblk][0] + ks * 16 * D * 2, vb[dblk][1] + ks * 16 * D * 2);
+          oacc[dblk] = mfma(a, pf[ks], oacc[dblk]);
+        }
+      sched_reads_ahead<kReadsAhead, 4 * (D / 32), 2>();
     }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d) oacc[d] *= alpha;
-      m_run = mn;
-    }
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, -m_run));
-        l_run += p;
-        pf[2 * kb + (r >> 3)][r & 7] = static_cast<__bf16>(p);
-      }
-    const char *vb[D / 32][2];
-#pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) vb[dblk][w] = opaque_lds(Vs + voff[dblk][w]);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int dblk = 0; dblk < D / 32; ++dblk) {
-        const bf16x8 a = ld_lds_tr_pair(vb[dblk][0] + ks * 16 * D * 2, vb[dblk][1] + ks * 16 * D * 2);
-        oacc[dblk] = mfma(a, pf[ks], oacc[dblk]);
-      }
-    sched_reads_ahead<kReadsAhead, 4 * (D / 32), 2>();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
