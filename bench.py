@@ -48,7 +48,7 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "74fb05afd9ae4850010816703af2f550491b7dc39d2f7ec2d1175ce666e33b68"
+TRAFFIC_SOURCES_SHA256 = "ce307cf09fd4062b4710ce0eb4cdf9d9cff3b7f26c41fc512810a4fa97c4e7e1"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
         "fwd": (1640152, 307972), "bwd_pre": (307992, 9784), "bwd_dq": (1805154, 303185),

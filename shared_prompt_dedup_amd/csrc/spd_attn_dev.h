@@ -122,10 +122,11 @@ __device__ inline void dma16(const void *base, unsigned voff, const char *lds) {
   const unsigned m = __builtin_amdgcn_readfirstlane(
       static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void *)(lds))));
   const void *b;
-  asm volatile("s_mov_b64 %0, %2\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0"
-               : "=&s"(b)
+  unsigned m0;   // M0 is an output of the assembly, not a clobber: the compiler knows it is written
+  asm volatile("s_mov_b64 %0, %3\n\ts_mov_b32 %1, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %0"
+               : "=&s"(b), "=&{m0}"(m0)
                : "v"(voff), "s"(base), "s"(m)
-               : "memory", "m0");
+               : "memory");
 }
 
 // Direct-to-LDS copy of rows [r0, r0 + ROWS) of a [*, H, D] bf16 tensor (head
