@@ -9,7 +9,7 @@
 //   phase B: keys [s0, r1) of the tile's own rows, visible iff
 //            seg_start[q] <= k <= q.
 //
-// Block: 8 waves (two per SIMD, so one wave's MFMAs overlap the other's
+// Block: 12 waves (three per SIMD, so two waves' MFMAs overlap the third's
 // softmax); wave w owns 32 query rows of one query head.  Per 64-key tile:
 // K and V are copied to LDS by direct-to-LDS loads (a pair of tiles is read
 // while the next pair loads, one barrier per pair), S^T = K Q^T puts one
@@ -25,7 +25,8 @@ namespace {
 
 using namespace dev;
 
-constexpr int kFwdWaves = 8;
+constexpr int kFwdWaves = 12;          // three waves per SIMD (at most 168 VGPRs each)
+constexpr int kFwdLoaders = 8;         // waves that issue the tile loads: a tile's 16-byte chunks split evenly over 8
 constexpr int kFwdBN = 64;
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kReadsAhead = 3;         // MFMAs an LDS operand read runs ahead of its use
@@ -102,14 +103,16 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
   const int n = nA + nB;
   auto kt_of = [&](int i) { return i < nA ? i * BN : t.s0 + (i - nA) * BN; };
 
+  constexpr int NL = kFwdLoaders;
   auto issue = [&](int i) {
+    if (wave >= NL) return;
     char *st = smem + (i % SLOTS) * 2 * TB;
     if (i < nA) {
-      dma_rows2<BN, D, NW>(st, k, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
-      dma_rows2<BN, D, NW>(st + TB, v, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
+      dma_rows2<BN, D, NL>(st, k, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
+      dma_rows2<BN, D, NL>(st + TB, v, kt_of(i), lenV, t.v0, t.u0, T, Hkv, kvh, wave, lane);
     } else {
-      dma_rows<BN, D, NW>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
-      dma_rows<BN, D, NW>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
+      dma_rows<BN, D, NL>(st, k, kt_of(i), T, Hkv, kvh, wave, lane);
+      dma_rows<BN, D, NL>(st + TB, v, kt_of(i), T, Hkv, kvh, wave, lane);
     }
   };
   wait_vm_all();
@@ -117,23 +120,27 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
 
   // One barrier per pair of tiles: past it, the pair's loads (issued a pair
   // ahead) have landed for every wave, and every wave is done with the
-  // previous pair, whose slots then take the next one.  Waves w and w + NW/2
-  // share a SIMD; at equal priority issue goes to the older, which would take
-  // every matrix-core slot it can use and then wait at the barrier while its
-  // partner ran alone.  So the older wave leads the pair's first tile
-  // (priority 2 over its partner's 1) and yields in the second (0).
-  const bool older = wave < NW / 2;
-  if (!older) set_prio<1>();
+  // previous pair, whose slots then take the next one.  Waves w, w + 4 and
+  // w + 8 share a SIMD; at equal priority issue goes to the oldest, which
+  // would take every matrix-core slot it can use and then wait at the barrier
+  // while the others ran on.  So the priorities rank the three by age in the
+  // pair's first tile (3, 2, 1) and in reverse in the second (1, 2, 3).
+  const int rank = wave / 4;   // 0: the oldest wave on its SIMD
   for (int j = 0; j < (n + 1) / 2; ++j) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (older) set_prio<2>();
+    if (rank == 0) set_prio<3>();
+    else if (rank == 1) set_prio<2>();
+    else set_prio<1>();
     if (2 * j + 2 < n) issue(2 * j + 2);
     if (2 * j + 3 < n) issue(2 * j + 3);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = 2 * j + u;
-      if (u == 1 && older) set_prio<0>();
+      if (u == 1) {
+        if (rank == 0) set_prio<1>();
+        else if (rank == 2) set_prio<3>();
+      }
       if (i >= n) break;
       const int kt = kt_of(i);
       const bool phaseA = i < nA;
