@@ -46,6 +46,14 @@ SMALL = {
                                resp_len_range=(5, 90), seed=43),
     "bf16_gqa3": _base.scaled(name="bf16_gqa3", num_prompts=2, rollout_n=2, prompt_len=70, response_len=30,
                               num_q_heads=3, num_kv_heads=1, head_dim=128, dtype="bf16", sigma=0.5, seed=37),
+    # one query head per kv head: the forward's tiles are 384 rows per head, so these prompts span several of
+    # them with a ragged last one (d 128 and d 64)
+    "bf16_gqa3_long": _base.scaled(name="bf16_gqa3_long", num_prompts=2, rollout_n=2, prompt_len=1100,
+                                   response_len=260, num_q_heads=3, num_kv_heads=1, head_dim=128, dtype="bf16",
+                                   sigma=0.5, resp_len_range=(50, 260), seed=44),
+    "bf16_mha_d64_long": _base.scaled(name="bf16_mha_d64_long", num_prompts=1, rollout_n=3, prompt_len=900,
+                                      response_len=200, num_q_heads=2, num_kv_heads=2, head_dim=64, dtype="bf16",
+                                      sigma=0.5, seed=45),
     # mid-size, every element compared: 2 prompts x 4 responses, prompt 2048, response 512, GQA 16/8/128
     "bf16_mid_2x4_p2048_r512": _base.scaled(name="bf16_mid_2x4_p2048_r512", num_prompts=2, rollout_n=4,
                                             prompt_len=2048, response_len=512, num_q_heads=16, num_kv_heads=8,
