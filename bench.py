@@ -48,12 +48,12 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "010ee2001d9c1917c26381b5c8c332882c3ed9a89ed11075a30cb299e991e494"
+TRAFFIC_SOURCES_SHA256 = "ba319b062ebccfa60ad0ebacf0274350bc2e08157e1108407605c2d1be63af91"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
-        "fwd": (1270982, 317796), "bwd_pre": (307993, 9784), "bwd_dq": (1805193, 303189),
-        "bwd_dkdv": (5129121, 303223), "reconstruct": (163433, 2162688), "pack_rows": (152799, 303187),
-        "reconstruct_bwd": (1070313, 303180), "pack_rows_bwd": (163234, 2162688),
+        "fwd": (1270410, 317775), "bwd_pre": (305800, 9784), "bwd_dq": (1805192, 303186),
+        "bwd_dkdv": (5235656, 303221), "reconstruct": (163431, 2162688), "pack_rows": (152799, 303188),
+        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163240, 2162688),
     },
 }
 
