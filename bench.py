@@ -48,7 +48,7 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "ba319b062ebccfa60ad0ebacf0274350bc2e08157e1108407605c2d1be63af91"
+TRAFFIC_SOURCES_SHA256 = "5c67edabde53785d197bf7c122330f1fa53b9ba7b091d0d5a91ebb5d1ea84c36"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
         "fwd": (1270410, 317775), "bwd_pre": (305800, 9784), "bwd_dq": (1805192, 303186),

@@ -12,14 +12,16 @@
 //   direct-to-LDS loads, S^T = K Q^T, dP^T = V dO^T, dq^T += K^T dS^T with
 //   K^T read by transposing LDS reads.  The wave raises its issue priority
 //   over its matrix-core phases, so they win ties against the other wave's
-//   softmax (1.4% faster; in k_dkdv the same marks cost 37% and are left out).
+//   softmax (about 2% faster than without).
 // k_dkdv: one block per 256-key tile and kv head; wave w owns keys
 //   [r0 + 32 w, r0 + 32 w + 32) for every query row.  K of a wave's keys stays
 //   in registers, V of the tile in LDS; Q and dO tiles of 64 query rows (plus
 //   their LSE, D and segment starts) arrive by direct-to-LDS loads, double
 //   buffered.  S = Q K^T and dP = dO V^T put one key per lane column, so P^T
 //   and dS^T feed dv += P^T dO and dk += dS^T Q directly, with dO^T and Q^T
-//   read by transposing LDS reads.  A tile the planner cut into chunks (a
+//   read by transposing LDS reads.  Of the two waves on a SIMD, the older
+//   leads each 64-row block's first half and the younger its second (issue
+//   priorities).  A tile the planner cut into chunks (a
 //   prompt or prefix key read by far more rows than a CU's fair share) leaves
 //   fp32 partial sums in numbered slots; an arrival counter per (tile, kv
 //   head) elects the last chunk to finish, which adds the slots in chunk
