@@ -48,12 +48,12 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "5c67edabde53785d197bf7c122330f1fa53b9ba7b091d0d5a91ebb5d1ea84c36"
+TRAFFIC_SOURCES_SHA256 = "4375a701fc69e596ed87990100194548029a7fb0be8795a923bac34b22befdc3"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
-        "fwd": (1270410, 317775), "bwd_pre": (305800, 9784), "bwd_dq": (1805192, 303186),
-        "bwd_dkdv": (5235656, 303221), "reconstruct": (163431, 2162688), "pack_rows": (152799, 303188),
-        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163240, 2162688),
+        "fwd": (1270374, 317800), "bwd_pre": (305796, 9784), "bwd_dq": (1803984, 303188),
+        "bwd_dkdv": (5151605, 303202), "reconstruct": (163455, 2162688), "pack_rows": (152799, 303188),
+        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163224, 2162688),
     },
 }
 

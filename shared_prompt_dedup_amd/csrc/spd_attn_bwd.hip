@@ -391,11 +391,15 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
     int h, qb, qend;
     bool masked;
     blk_of(i, h, qb, masked, qend);
+    // The younger wave of each SIMD issues the loads, each two waves' share:
+    // the older leads the block's first half and starts its MFMAs at once.
+    const int lw = wave - NW / 2;
+    if (lw < 0) return;
     char *st = smem + (i % STAGES) * STAGE;
-    dma_rows<QB, D, NW>(st, q, qb, T, Hq, h, wave, lane);
-    dma_rows<QB, D, NW>(st + TB, dout, qb, T, Hq, h, wave, lane);
-    if (wave == 0) dma_scalars(st + 2 * TB, Lbuf + int64_t(h) * Tp + qb, lane);
-    if (wave == 1) dma_scalars(st + 2 * TB + 256, Dbuf + int64_t(h) * Tp + qb, lane);
+    dma_rows<QB, D, NW / 2>(st, q, qb, T, Hq, h, lw, lane);
+    dma_rows<QB, D, NW / 2>(st + TB, dout, qb, T, Hq, h, lw, lane);
+    if (lw == 0) dma_scalars(st + 2 * TB, Lbuf + int64_t(h) * Tp + qb, lane);
+    if (lw == 1) dma_scalars(st + 2 * TB + 256, Dbuf + int64_t(h) * Tp + qb, lane);
   };
 
   // Waves w and w + NW / 2 share a SIMD, and at equal priority issue goes to
@@ -407,8 +411,8 @@ __global__ void __launch_bounds__(kWaves * 64) k_dkdv(const Tile *__restrict__ t
   if (!older) set_prio<1>();
   for (int i = 0; i < STAGES - 1 && i < n; ++i) issue(i);
   for (int i = 0; i < n; ++i) {
-    // waves 0-1 issue one extra load per block: waiting for PER-sized stages
-    // only makes them wait longer, never too little
+    // with two stages the ring waits for every load of the issuing waves
+    static_assert(STAGES == 2, "the loading waves issue two waves' share: a deeper ring needs its own count");
     wait_ring<STAGES, PER>(i, n);
     if (older) set_prio<2>();
     if (i + STAGES - 1 < n) issue(i + STAGES - 1);
