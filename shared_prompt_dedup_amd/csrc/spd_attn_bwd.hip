@@ -165,7 +165,8 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
   const int seg_q = qvalid ? seg_start[qrow] : 0x7fffffff;
   const int seg_hi = qlast >= qw0 ? seg_start[qlast] : 0x7fffffff;
   // P = exp2(c s + s_bias), dS = P (dP + dp_bias) with s_bias = -c lse/scale
-  // = -lse log2(e) and dp_bias = -D (the arrays hold -lse/scale and -D)
+  // = -lse log2(e) and dp_bias = -D (the arrays hold -lse/scale and -D); the
+  // dP accumulator starts at dp_bias, so the MFMA adds it
   const float s_bias = qvalid ? Lbuf[int64_t(h) * Tp + qrow] * scale_log2 : 0.0f;
   const float dp_bias = qvalid ? Dbuf[int64_t(h) * Tp + qrow] : 0.0f;
 
@@ -236,7 +237,9 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
       for (int w = 0; w < 2; ++w) kb_[dblk][w] = opaque_lds(Ks + toff[dblk][w]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
+      f32x16 s = zero16(), dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = dp_bias;   // the dP accumulator starts at -D
       __builtin_amdgcn_s_setprio(1);   // matrix-core phases win issue ties against the other wave's softmax
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -258,7 +261,7 @@ __global__ void __launch_bounds__(kWaves * 64) k_dq(const Tile *__restrict__ til
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, s_bias));
-        dsf[r >> 3][r & 7] = static_cast<__bf16>(p * (dp[r] + dp_bias));
+        dsf[r >> 3][r & 7] = static_cast<__bf16>(p * dp[r]);
       }
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
