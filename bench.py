@@ -48,12 +48,12 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 TRAFFIC_SOURCES = ("spd_attn.h", "spd_attn_dev.h", "spd_attn_api.hip", "spd_attn_fwd.hip", "spd_attn_bwd.hip",
                    "spd_internal.h", "spd_dedup.hip")
-TRAFFIC_SOURCES_SHA256 = "031868b59177e39dcde683f0c7424ce9a3dc6338e9561150c0a20d2ad18d8a77"
+TRAFFIC_SOURCES_SHA256 = "bb06d9c9f236dc2d0c97683468fbcaee33bb538e13262d0e92214e6828262a7b"
 TRAFFIC_KIB = {   # workload -> kernel -> (FETCH_SIZE KiB, WRITE_SIZE KiB) per dispatch, uncalibrated
     "long_2x8_p32768_r256to1024_unpad": {
-        "fwd": (1269458, 317800), "bwd_pre": (305796, 9784), "bwd_dq": (1804649, 303184),
-        "bwd_dkdv": (5006857, 303217), "reconstruct": (163470, 2162688), "pack_rows": (152799, 303190),
-        "reconstruct_bwd": (1070312, 303181), "pack_rows_bwd": (163233, 2162688),
+        "fwd": (1271923, 318043), "bwd_pre": (305777, 9784), "bwd_dq": (1804535, 303184),
+        "bwd_dkdv": (5037939, 303206), "reconstruct": (163459, 2162688), "pack_rows": (152799, 303190),
+        "reconstruct_bwd": (1070312, 303180), "pack_rows_bwd": (163248, 2162688),
     },
 }
 

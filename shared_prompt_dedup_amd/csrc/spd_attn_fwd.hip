@@ -118,13 +118,16 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
   wait_vm_all();
   for (int i = 0; i < 2 && i < n; ++i) issue(i);
 
-  // One barrier per pair of tiles: past it, the pair's loads (issued a pair
-  // ahead) have landed for every wave, and every wave is done with the
-  // previous pair, whose slots then take the next one.  Waves w, w + 4 and
-  // w + 8 share a SIMD; at equal priority issue goes to the oldest, which
-  // would take every matrix-core slot it can use and then wait at the barrier
-  // while the others ran on.  So the priorities rank the three by age in the
-  // pair's first tile (3, 2, 1) and in reverse in the second (1, 2, 3).
+  // One barrier per pair of tiles: past it, the pair's loads (issued during
+  // the previous pair) have landed for every wave, and every wave is done with
+  // the previous pair, whose slots then take the next one.  The next pair's
+  // first tile is issued right after the barrier, its second between this
+  // pair's two tiles, so the loading waves stall on half the burst at a time.
+  // Waves w, w + 4 and w + 8 share a SIMD; at equal priority issue goes to
+  // the oldest, which would take every matrix-core slot it can use and then
+  // wait at the barrier while the others ran on.  So the priorities rank the
+  // three by age in the pair's first tile (3, 2, 1) and in reverse in the
+  // second (1, 2, 3).
   const int rank = wave / 4;   // 0: the oldest wave on its SIMD
   for (int j = 0; j < (n + 1) / 2; ++j) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -133,13 +136,13 @@ __global__ void __launch_bounds__(kFwdWaves * 64) k_fwd(const Tile *__restrict__
     else if (rank == 1) set_prio<2>();
     else set_prio<1>();
     if (2 * j + 2 < n) issue(2 * j + 2);
-    if (2 * j + 3 < n) issue(2 * j + 3);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = 2 * j + u;
       if (u == 1) {
         if (rank == 0) set_prio<1>();
         else if (rank == 2) set_prio<3>();
+        if (2 * j + 3 < n) issue(2 * j + 3);
       }
       if (i >= n) break;
       const int kt = kt_of(i);
