@@ -54,6 +54,10 @@ SMALL = {
     "bf16_mha_d64_long": _base.scaled(name="bf16_mha_d64_long", num_prompts=1, rollout_n=3, prompt_len=900,
                                       response_len=200, num_q_heads=2, num_kv_heads=2, head_dim=64, dtype="bf16",
                                       sigma=0.5, seed=45),
+    # eight query heads per kv head: the forward takes four per block, 96-row tiles, several per prompt
+    "bf16_gqa8_d64_long": _base.scaled(name="bf16_gqa8_d64_long", num_prompts=2, rollout_n=2, prompt_len=700,
+                                       response_len=150, num_q_heads=8, num_kv_heads=1, head_dim=64, dtype="bf16",
+                                       sigma=0.5, resp_len_range=(20, 150), seed=46),
     # mid-size, every element compared: 2 prompts x 4 responses, prompt 2048, response 512, GQA 16/8/128
     "bf16_mid_2x4_p2048_r512": _base.scaled(name="bf16_mid_2x4_p2048_r512", num_prompts=2, rollout_n=4,
                                             prompt_len=2048, response_len=512, num_q_heads=16, num_kv_heads=8,
