@@ -32,8 +32,9 @@
  *   queries.
  * - Every call is asynchronous on the given stream (a hipStream_t passed as
  *   void*; NULL = the null stream) and keeps no state between calls (apart
- *   from the opt-in, per-thread kernel timing at the end of this header), so
- *   calls on different streams may run concurrently on disjoint buffers.
+ *   from the opt-in, per-thread kernel timing at the end of this header and
+ *   the fixed scratch array of spd_split_attn_fwd_noalloc), so calls on
+ *   different streams may run concurrently on disjoint buffers.
  * - Arguments are validated on the host before anything is launched; a
  *   non-zero spd_status is returned and nothing runs.  SPD_ERR_HIP means a
  *   launch failed (hipGetLastError after the launch); spd_last_hip_error()
